@@ -1,0 +1,92 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins catch each.
+
+Each mutant replaces one oracle function for the duration of a test; the listed pins must
+then fail.  This shows the pins constrain the parts of the oracle they are meant to.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.dirname(__file__))
+
+from oracle import attention as A
+import test_oracle_pins as pins
+
+_orig_visibility = A.visibility
+_orig_backward_head = A.backward_head
+_orig_merge = A.merge_states
+_orig_forward_head = A.forward_head
+
+
+def vis_strict_causal(seg_q, seg_k, q_offset=0, k_offset=0, causal=True):
+    m = _orig_visibility(seg_q, seg_k, q_offset, k_offset, causal)
+    if causal:
+        qpos = q_offset + np.arange(len(seg_q))
+        kpos = k_offset + np.arange(len(seg_k))
+        m &= kpos[None, :] < qpos[:, None]
+    return m
+
+
+def vis_ignores_segments(seg_q, seg_k, q_offset=0, k_offset=0, causal=True):
+    z = np.zeros(len(seg_q), np.int32), np.zeros(len(seg_k), np.int32)
+    return _orig_visibility(z[0], z[1], q_offset, k_offset, causal)
+
+
+def bwd_drops_delta(q, k, v, do, mask, scale):
+    o, _, p = A.forward_head(q, k, v, mask, scale)
+    dp = do @ v.T
+    ds = p * dp
+    return scale * ds @ k, scale * ds.T @ q, p.T @ do
+
+
+def bwd_unscaled_dk(q, k, v, do, mask, scale):
+    dq, dk, dv = _orig_backward_head(q, k, v, do, mask, scale)
+    return dq, dk / scale, dv
+
+
+def bwd_wrong_dv_operand(q, k, v, do, mask, scale):
+    dq, dk, dv = _orig_backward_head(q, k, v, do, mask, scale)
+    o, _, p = A.forward_head(q, k, v, mask, scale)
+    return dq, dk, p.T @ o
+
+
+def merge_same_weight(a, b):
+    m1, l1, acc1 = a
+    m2, l2, acc2 = b
+    m = np.maximum(m1, m2)
+    fin = np.isfinite(m)
+    w = np.where(fin, np.exp(np.where(np.isfinite(m1), m1, 0) - np.where(fin, m, 0)), 0.0)
+    w = np.where(np.isfinite(m1), w, 0.0)
+    return np.where(fin, m, -np.inf), l1 * w + l2 * w, acc1 * w[:, None] + acc2 * w[:, None]
+
+
+def fwd_lse_without_log(q, k, v, mask, scale):
+    o, lse, p = _orig_forward_head(q, k, v, mask, scale)
+    s = np.where(mask, scale * (q @ k.T), -np.inf)
+    m = s.max(axis=1)
+    return o, np.where(np.isfinite(lse), m + np.exp(lse - m), lse), p
+
+
+MUTANTS = [
+    ("visibility", vis_strict_causal,
+     [lambda: pins.test_brute_force_tiny(0), lambda: pins.test_matches_torch_sdpa_float64("single_causal")]),
+    ("visibility", vis_ignores_segments,
+     [lambda: pins.test_q_zero_gives_segment_prefix_mean(0), pins.test_packed_equals_per_segment]),
+    ("backward_head", bwd_drops_delta, [pins.test_finite_difference_gradients]),
+    ("backward_head", bwd_unscaled_dk, [pins.test_finite_difference_gradients]),
+    ("backward_head", bwd_wrong_dv_operand, [pins.test_finite_difference_gradients]),
+    ("merge_states", merge_same_weight, [pins.test_ring_order_merge_equals_full]),
+    ("forward_head", fwd_lse_without_log,
+     [lambda: pins.test_blockwise_equals_one_shot(64), lambda: pins.test_q_zero_gives_segment_prefix_mean(1)]),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(MUTANTS)))
+def test_pins_catch_mutant(idx, monkeypatch):
+    name, mutant, checks = MUTANTS[idx]
+    monkeypatch.setattr(A, name, mutant)
+    for check in checks:
+        with pytest.raises(AssertionError):
+            check()
