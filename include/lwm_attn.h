@@ -1,0 +1,170 @@
+/*
+ * lwm_attn.h -- C-ABI of the MI355X (gfx950) exact blockwise causal attention library.
+ *
+ * What the calls compute.  Exact softmax attention, not windowed and not sparse, over a
+ * sequence that may hold several packed samples.  The LWM pages state the three parts:
+ *   - exact full attention at million-token length, evaluated block by block with
+ *     key/value blocks arriving from a device ring: LWM deep dive, section
+ *     "RingAttention 为什么必要" (why RingAttention is necessary);
+ *   - a causal next-token model over one unified token sequence: same page, sections
+ *     "核心问题" (core problem) and "模型结构" (model structure, "Training objective");
+ *   - packed samples that only attend to themselves: same page, section
+ *     "Masked sequence packing", first step of the LWM recipe.
+ * The pages give no formula; the library uses the textbook reading.  For query row i
+ * (global position q_offset + i) and key j (global position k_offset + j):
+ *   visible(i,j) = seg_q[i] >= 0 && seg_q[i] == seg_k[j] && (!causal || k_offset+j <= q_offset+i)
+ *   s_ij = scale * <q_i, k_j>,   P_i = softmax over visible j,   O_i = sum_j P_ij v_j,
+ *   LSE_i = max_j s_ij + ln(sum_j exp(s_ij - max_j s_ij))   (natural log)
+ * A row with no visible key has O = 0 and LSE = -inf.
+ *
+ * Conventions for every call:
+ *   - Tensors are dense and contiguous: Q, O, dO, dQ are [B,H,Sq,D]; K, V, dK, dV are
+ *     [B,H,Sk,D]; D is innermost.  LSE, m, l are float32 [B,H,Sq]; the partial
+ *     accumulator is float32 [B,H,Sq,D].  Segment ids are int32 [B,Sq] / [B,Sk], shared by
+ *     all heads.  A negative segment id marks padding: it sees nothing and nothing sees it.
+ *   - Every pointer is a device pointer owned by the caller; the library never allocates,
+ *     frees or synchronises, and keeps no mutable global state.  `stream` is a hipStream_t
+ *     (NULL = the null stream); every call only enqueues work on it and returns.
+ *   - Device pointers must be 16-byte aligned.  All arguments are validated on the host
+ *     before anything is enqueued; on error nothing is enqueued.
+ *   - Return value: LWM_OK (0) or a negative LWM_ERR_* code; lwm_attn_status_string()
+ *     names it.  LWM_ERR_HIP reports a failed kernel launch (hipGetLastError).
+ *   - NaN or Inf in the inputs is propagated, not checked.
+ */
+#ifndef LWM_ATTN_H
+#define LWM_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { LWM_BF16 = 0, LWM_F32 = 1 } lwm_dtype;
+
+/* FINAL writes the normalised output O and LSE.  PARTIAL writes the unnormalised state
+ * (m, l, acc) of the keys given, for later merging with lwm_attn_merge_chunk. */
+typedef enum { LWM_OUT_FINAL = 0, LWM_OUT_PARTIAL = 1 } lwm_out_mode;
+
+enum {
+  LWM_OK = 0,
+  LWM_ERR_INVALID_ARG = -1, /* NULL pointer, bad enum, negative size, bad block size   */
+  LWM_ERR_SHAPE = -2,       /* inconsistent or overflowing sizes                        */
+  LWM_ERR_ALIGNMENT = -3,   /* a device pointer is not 16-byte aligned                   */
+  LWM_ERR_UNSUPPORTED = -4, /* dtype / head width / block size combination not built     */
+  LWM_ERR_WORKSPACE = -5,   /* workspace missing or smaller than the size query returns */
+  LWM_ERR_HIP = -6          /* a kernel launch failed                                    */
+};
+
+/* Tile classes stored in the block table. */
+enum { LWM_TILE_SKIP = 0, LWM_TILE_PARTIAL = 1, LWM_TILE_FULL = 2 };
+
+typedef struct {
+  int32_t B, H, Sq, Sk, D; /* Q [B,H,Sq,D]; K,V [B,H,Sk,D]                               */
+  int64_t q_offset;        /* global position of query row 0 (ring share); else 0       */
+  int64_t k_offset;        /* global position of key row 0 (ring share); else 0         */
+  float scale;             /* score scale, e.g. 1/sqrt(D)                                */
+  int32_t causal;          /* 1: key visible only if its global position <= the query's */
+  int32_t block_q;         /* query rows per table block (the query-chunk size knob)   */
+  int32_t block_k;         /* keys per table block                                      */
+  int32_t dtype;           /* lwm_dtype of Q, K, V, O, dO, dQ, dK, dV                    */
+} lwm_attn_desc;
+
+/*
+ * Block table.  Classifies each (query block, key block) pair so the kernels can skip
+ * pairs with no visible key and drop masking where every pair is visible; it is how the
+ * causal and packing masks of the pages become skipped work.
+ *   status  uint8 [B][nqb][nkb]: LWM_TILE_SKIP if no pair can be visible (causally empty,
+ *           all padding, or disjoint segment-id intervals), LWM_TILE_FULL if the block lies
+ *           inside [0,Sq)x[0,Sk) and every pair is visible, else LWM_TILE_PARTIAL.
+ *           SKIP is exact when segment ids are non-decreasing along the sequence (what
+ *           packing produces) and conservative (never wrong) for any ids.
+ *   q_range int32 [B][nqb][2]: first and last non-SKIP key block of each query block
+ *           (first > last when there is none).
+ *   k_range int32 [B][nkb][2]: first and last non-SKIP query block of each key block.
+ * with nqb = ceil(Sq/block_q), nkb = ceil(Sk/block_k).  Buffer layout: q_range, then
+ * k_range, then status, then per-block segment statistics the builder uses internally,
+ * each part starting on a 256-byte boundary; lwm_attn_block_table_bytes gives the total.
+ * block_q and block_k must each be 16, 32 or 64; the attention kernels need 64 x 64.
+ * The table depends on desc (B, Sq, Sk, offsets, causal, blocks) and the segment ids only.
+ */
+size_t lwm_attn_block_table_bytes(const lwm_attn_desc* desc);
+int lwm_attn_build_block_table(const lwm_attn_desc* desc, const int32_t* seg_q,
+                               const int32_t* seg_k, void* table, void* stream);
+
+/*
+ * Forward attention of Q against the keys K, V given (one KV chunk or the whole sequence).
+ * This is one query block's pass over streamed key/value blocks of the pages' blockwise
+ * (ring) attention, with a running max, denominator and accumulator per query row.
+ *   mode FINAL:   o [B,H,Sq,D] (desc dtype) and lse float32 [B,H,Sq]; m, l, acc unused.
+ *   mode PARTIAL: m, l float32 [B,H,Sq] and acc float32 [B,H,Sq,D] such that
+ *                 l = sum_j exp(s_ij - m), acc = sum_j exp(s_ij - m) v_j over the visible
+ *                 keys given; a row with none gets (m, l, acc) = (-inf, 0, 0).
+ *                 m is finite whenever l > 0 but need not equal max_j s_ij; o, lse unused.
+ * Supported: dtype LWM_BF16 with D = 128 (bf16 MFMA, float32 accumulation) and
+ * LWM_F32 with D in {32, 64}; table built with block_q = block_k = 64.
+ */
+int lwm_attn_fwd(const lwm_attn_desc* desc, int32_t mode, const void* q, const void* k,
+                 const void* v, const int32_t* seg_q, const int32_t* seg_k, const void* table,
+                 void* o, float* lse, float* m, float* l, float* acc, void* stream);
+
+/*
+ * Merge a chunk's partial state into a running state (the ring step's combine): per row
+ *   m' = max(m, mc),  l' = l e^(m-m') + lc e^(mc-m'),  acc' = acc e^(m-m') + accc e^(mc-m').
+ * An empty side (l = 0) contributes nothing; two empty sides stay empty (-inf, 0, 0).
+ * rows = B*H*Sq; m, l, mc, lc are float32 [rows]; acc, accc float32 [rows, D].
+ *   finalize = 0: the merged state is written back to m, l, acc; o and lse are unused.
+ *   finalize = 1: o [rows, D] (out_dtype) = acc'/l' and lse [rows] = m' + ln l' are
+ *                 written and m, l, acc are left unchanged.  mc, lc, accc may all be NULL
+ *                 to finalize the running state alone.
+ * D must be a multiple of 4 and at most 256.
+ */
+int lwm_attn_merge_chunk(int64_t rows, int32_t D, float* m, float* l, float* acc,
+                         const float* mc, const float* lc, const float* accc, int32_t finalize,
+                         int32_t out_dtype, void* o, float* lse, void* stream);
+
+/*
+ * Backward of the forward above for an upstream gradient dO, recomputing P from the saved
+ * LSE (P_ij = exp(s_ij - LSE_i) on visible pairs):
+ *   Delta_i = <dO_i, O_i>,  dS_ij = P_ij (<dO_i, v_j> - Delta_i),
+ *   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i,
+ * sums running over the keys given and the queries given.  o and lse are the forward's
+ * outputs for the same rows (for a ring share: the outputs after all chunks were merged,
+ * and dq is then this chunk's contribution).  dq, dk, dv are written (not accumulated).
+ * workspace: device memory of at least lwm_attn_bwd_workspace_bytes(desc) bytes, owned by
+ * the caller; its contents on entry do not matter.
+ * Supported combinations are those of lwm_attn_fwd.
+ */
+size_t lwm_attn_bwd_workspace_bytes(const lwm_attn_desc* desc);
+int lwm_attn_bwd(const lwm_attn_desc* desc, const void* q, const void* k, const void* v,
+                 const void* o, const void* dO, const float* lse, const int32_t* seg_q,
+                 const int32_t* seg_k, const void* table, void* dq, void* dk, void* dv,
+                 void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * One phase of lwm_attn_bwd, same arguments and buffers.  The phases in order:
+ *   LWM_BWD_DELTA  Delta = rowsum(dO * O) into the workspace;
+ *   LWM_BWD_DQ     dq from Delta (query-major pass over key tiles);
+ *   LWM_BWD_DKV    dk, dv from Delta (key-major pass over query tiles).
+ * DQ and DKV read the workspace DELTA wrote and are independent of each other, so a caller
+ * may run them on two streams once DELTA has completed.  lwm_attn_bwd runs all three on
+ * one stream.  For Sq == 0 or Sk == 0 the DQ / DKV phases zero their outputs.
+ */
+enum { LWM_BWD_DELTA = 0, LWM_BWD_DQ = 1, LWM_BWD_DKV = 2 };
+int lwm_attn_bwd_phase(const lwm_attn_desc* desc, int32_t phase, const void* q, const void* k,
+                       const void* v, const void* o, const void* dO, const float* lse,
+                       const int32_t* seg_q, const int32_t* seg_k, const void* table, void* dq,
+                       void* dk, void* dv, void* workspace, size_t ws_bytes, void* stream);
+
+/* Static, NUL-terminated name of a status code. */
+const char* lwm_attn_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int lwm_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LWM_ATTN_H */

@@ -1,0 +1,311 @@
+"""MI355X (gfx950) exact blockwise causal attention with ring-order merging and masked
+sequence packing.
+
+Thin ctypes binding over the C-ABI library `liblwm_attn.so` (include/lwm_attn.h).  The
+functions named `lwm_attn_*` mirror the C entry points one to one and only marshal
+arguments: torch tensors supply device memory and the current HIP stream, every
+computation runs in the library's HIP kernels.  There is no CPU fallback: if the library
+is missing or no GPU is present the calls raise.
+
+Convenience layers on top of those calls:
+  attention_forward / attention_backward -- table + forward (+ backward) for one sequence
+  ring_share_forward                      -- one device's share of the LWM ring: a query
+                                             chunk merged against KV chunks in ring order
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import List, Optional, Sequence, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblwm_attn.so")
+
+LWM_BF16, LWM_F32 = 0, 1
+LWM_OUT_FINAL, LWM_OUT_PARTIAL = 0, 1
+LWM_TILE_SKIP, LWM_TILE_PARTIAL, LWM_TILE_FULL = 0, 1, 2
+TABLE_BLOCK = 64
+
+STATUS = {
+    0: "LWM_OK", -1: "LWM_ERR_INVALID_ARG", -2: "LWM_ERR_SHAPE", -3: "LWM_ERR_ALIGNMENT",
+    -4: "LWM_ERR_UNSUPPORTED", -5: "LWM_ERR_WORKSPACE", -6: "LWM_ERR_HIP",
+}
+
+EXPORTED = (
+    "lwm_attn_block_table_bytes", "lwm_attn_build_block_table", "lwm_attn_fwd",
+    "lwm_attn_merge_chunk", "lwm_attn_bwd_workspace_bytes", "lwm_attn_bwd",
+    "lwm_attn_bwd_phase", "lwm_attn_status_string", "lwm_attn_version",
+)
+LWM_BWD_DELTA, LWM_BWD_DQ, LWM_BWD_DKV = 0, 1, 2
+
+
+class LwmError(RuntimeError):
+    def __init__(self, call: str, status: int, message: str):
+        super().__init__(f"{call} failed with {status}: {message}")
+        self.status = status
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Sq", ctypes.c_int32),
+        ("Sk", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("q_offset", ctypes.c_int64), ("k_offset", ctypes.c_int64),
+        ("scale", ctypes.c_float), ("causal", ctypes.c_int32),
+        ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32), ("dtype", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the shared library (once) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m long_context_exact_blockwise_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    DP = ctypes.POINTER(Desc)
+    sig = {
+        "lwm_attn_block_table_bytes": (SZ, [DP]),
+        "lwm_attn_build_block_table": (ctypes.c_int, [DP, P, P, P, P]),
+        "lwm_attn_fwd": (ctypes.c_int, [DP, I32, P, P, P, P, P, P, P, P, P, P, P, P]),
+        "lwm_attn_merge_chunk": (ctypes.c_int, [I64, I32, P, P, P, P, P, P, I32, I32, P, P, P]),
+        "lwm_attn_bwd_workspace_bytes": (SZ, [DP]),
+        "lwm_attn_bwd": (ctypes.c_int, [DP, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "lwm_attn_bwd_phase": (ctypes.c_int, [DP, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "lwm_attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "lwm_attn_version": (ctypes.c_int, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(call: str, rc: int):
+    if rc != 0:
+        msg = load_library().lwm_attn_status_string(rc).decode()
+        raise LwmError(call, rc, msg)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("lwm_attn: tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("lwm_attn: tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> Optional[int]:
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dtype_code(dtype) -> int:
+    import torch
+
+    if dtype == torch.bfloat16:
+        return LWM_BF16
+    if dtype == torch.float32:
+        return LWM_F32
+    raise ValueError(f"unsupported dtype {dtype}")
+
+
+def make_desc(B, H, Sq, Sk, D, dtype, *, scale=None, causal=True, q_offset=0, k_offset=0,
+              block_q=TABLE_BLOCK, block_k=TABLE_BLOCK) -> Desc:
+    return Desc(B, H, Sq, Sk, D, int(q_offset), int(k_offset),
+                float(1.0 / math.sqrt(D) if scale is None else scale), int(bool(causal)),
+                int(block_q), int(block_k), _dtype_code(dtype) if not isinstance(dtype, int) else dtype)
+
+
+# ---------------------------------------------------------------------------------------
+# one-to-one wrappers of the C entry points
+# ---------------------------------------------------------------------------------------
+
+def lwm_attn_block_table_bytes(desc: Desc) -> int:
+    return int(load_library().lwm_attn_block_table_bytes(ctypes.byref(desc)))
+
+
+def lwm_attn_build_block_table(desc: Desc, seg_q, seg_k, table=None, stream=None):
+    """Builds the block table into `table` (uint8 device tensor; allocated when None)."""
+    import torch
+
+    n = lwm_attn_block_table_bytes(desc)
+    if table is None:
+        table = torch.empty(max(n, 16), dtype=torch.uint8, device=seg_q.device)
+    elif table.numel() * table.element_size() < n:
+        raise ValueError("table buffer too small")
+    rc = load_library().lwm_attn_build_block_table(ctypes.byref(desc), _ptr(seg_q), _ptr(seg_k),
+                                                   _ptr(table), _stream(stream))
+    _check("lwm_attn_build_block_table", rc)
+    return table
+
+
+def lwm_attn_fwd(desc: Desc, mode: int, q, k, v, seg_q, seg_k, table, o=None, lse=None, m=None,
+                 l=None, acc=None, stream=None):
+    rc = load_library().lwm_attn_fwd(ctypes.byref(desc), int(mode), _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(seg_q), _ptr(seg_k), _ptr(table), _ptr(o), _ptr(lse),
+                                     _ptr(m), _ptr(l), _ptr(acc), _stream(stream))
+    _check("lwm_attn_fwd", rc)
+
+
+def lwm_attn_merge_chunk(rows: int, D: int, m, l, acc, mc=None, lc=None, accc=None,
+                         finalize: bool = False, out_dtype: int = LWM_BF16, o=None, lse=None,
+                         stream=None):
+    rc = load_library().lwm_attn_merge_chunk(int(rows), int(D), _ptr(m), _ptr(l), _ptr(acc),
+                                             _ptr(mc), _ptr(lc), _ptr(accc), int(bool(finalize)),
+                                             int(out_dtype), _ptr(o), _ptr(lse), _stream(stream))
+    _check("lwm_attn_merge_chunk", rc)
+
+
+def lwm_attn_bwd_workspace_bytes(desc: Desc) -> int:
+    return int(load_library().lwm_attn_bwd_workspace_bytes(ctypes.byref(desc)))
+
+
+def lwm_attn_bwd(desc: Desc, q, k, v, o, do, lse, seg_q, seg_k, table, dq, dk, dv, workspace,
+                 stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load_library().lwm_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                     _ptr(do), _ptr(lse), _ptr(seg_q), _ptr(seg_k), _ptr(table),
+                                     _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes,
+                                     _stream(stream))
+    _check("lwm_attn_bwd", rc)
+
+
+def lwm_attn_bwd_phase(desc: Desc, phase: int, q, k, v, o, do, lse, seg_q, seg_k, table, dq, dk,
+                       dv, workspace, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load_library().lwm_attn_bwd_phase(ctypes.byref(desc), int(phase), _ptr(q), _ptr(k),
+                                           _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(seg_q),
+                                           _ptr(seg_k), _ptr(table), _ptr(dq), _ptr(dk), _ptr(dv),
+                                           _ptr(workspace), ws_bytes, _stream(stream))
+    _check("lwm_attn_bwd_phase", rc)
+
+
+# ---------------------------------------------------------------------------------------
+# convenience layers (allocation with torch, then the calls above)
+# ---------------------------------------------------------------------------------------
+
+def _desc_for(q, k, *, scale, causal, q_offset, k_offset):
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    return make_desc(B, H, Sq, Sk, D, q.dtype, scale=scale, causal=causal, q_offset=q_offset,
+                     k_offset=k_offset)
+
+
+def attention_forward(q, k, v, seg_q, seg_k, *, scale=None, causal=True, q_offset=0, k_offset=0,
+                      table=None, stream=None):
+    """(O, LSE, table) for Q [B,H,Sq,D] against K, V [B,H,Sk,D] with segment ids."""
+    import torch
+
+    desc = _desc_for(q, k, scale=scale, causal=causal, q_offset=q_offset, k_offset=k_offset)
+    if table is None:
+        table = lwm_attn_build_block_table(desc, seg_q, seg_k, stream=stream)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    lwm_attn_fwd(desc, LWM_OUT_FINAL, q, k, v, seg_q, seg_k, table, o=o, lse=lse, stream=stream)
+    return o, lse, table
+
+
+def attention_partial(q, k, v, seg_q, seg_k, *, scale=None, causal=True, q_offset=0, k_offset=0,
+                      table=None, out=None, stream=None):
+    """(m, l, acc) state of Q against one KV chunk."""
+    import torch
+
+    desc = _desc_for(q, k, scale=scale, causal=causal, q_offset=q_offset, k_offset=k_offset)
+    if table is None:
+        table = lwm_attn_build_block_table(desc, seg_q, seg_k, stream=stream)
+    B, H, Sq, D = q.shape
+    if out is None:
+        m = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+        l = torch.empty_like(m)
+        acc = torch.empty((B, H, Sq, D), dtype=torch.float32, device=q.device)
+    else:
+        m, l, acc = out
+    lwm_attn_fwd(desc, LWM_OUT_PARTIAL, q, k, v, seg_q, seg_k, table, m=m, l=l, acc=acc,
+                 stream=stream)
+    return m, l, acc
+
+
+def attention_backward(q, k, v, o, do, lse, seg_q, seg_k, table, *, scale=None, causal=True,
+                       q_offset=0, k_offset=0, workspace=None, stream=None):
+    """(dQ, dK, dV) by LSE recompute."""
+    import torch
+
+    desc = _desc_for(q, k, scale=scale, causal=causal, q_offset=q_offset, k_offset=k_offset)
+    if workspace is None:
+        workspace = torch.empty(max(lwm_attn_bwd_workspace_bytes(desc), 16), dtype=torch.uint8,
+                                device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    lwm_attn_bwd(desc, q, k, v, o, do, lse, seg_q, seg_k, table, dq, dk, dv, workspace,
+                 stream=stream)
+    return dq, dk, dv
+
+
+def ring_order(rank: int, n_chunks: int) -> List[int]:
+    """KV chunk held by device `rank` at each ring step when chunks travel one device per
+    step towards higher ranks: at step t the device holds chunk (rank - t) mod N."""
+    return [(rank - t) % n_chunks for t in range(n_chunks)]
+
+
+def ring_share_forward(q, k_chunks: Sequence, v_chunks: Sequence, seg_q, seg_k_chunks: Sequence,
+                       *, q_offset: int, chunk_offsets: Sequence[int], order: Sequence[int],
+                       scale=None, causal=True, tables=None, states=None, stream=None):
+    """One device's share of the ring: the query chunk Q (global offset q_offset) merged
+    against the KV chunks in `order`.  Chunks whose keys all lie after the last query are
+    skipped on the host (they contribute nothing under the causal mask).  The first
+    contributing chunk writes the running state; each later one writes a chunk state that
+    lwm_attn_merge_chunk folds in; the last merge finalises into (O, LSE).
+
+    `tables` (optional) maps chunk index -> prebuilt table; `states` (optional) is a pair
+    of preallocated (m, l, acc) triples.  Returns (O, LSE, tables)."""
+    import torch
+
+    B, H, Sq, D = q.shape
+    last_q = q_offset + Sq - 1
+    live = [c for c in order if not (causal and chunk_offsets[c] > last_q)]
+    tables = {} if tables is None else tables
+    if states is None:
+        mk = lambda: (torch.empty((B, H, Sq), dtype=torch.float32, device=q.device),
+                      torch.empty((B, H, Sq), dtype=torch.float32, device=q.device),
+                      torch.empty((B, H, Sq, D), dtype=torch.float32, device=q.device))
+        states = (mk(), mk())
+    run, chunk = states
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    rows = B * H * Sq
+    odt = _dtype_code(q.dtype)
+    if not live:
+        # every chunk is in the future: empty state finalises to O = 0, LSE = -inf
+        run[0].fill_(float("-inf"))
+        run[1].zero_()
+        run[2].zero_()
+        lwm_attn_merge_chunk(rows, D, *run, finalize=True, out_dtype=odt, o=o, lse=lse,
+                             stream=stream)
+        return o, lse, tables
+    for step, c in enumerate(live):
+        desc = _desc_for(q, k_chunks[c], scale=scale, causal=causal, q_offset=q_offset,
+                         k_offset=chunk_offsets[c])
+        if c not in tables:
+            tables[c] = lwm_attn_build_block_table(desc, seg_q, seg_k_chunks[c], stream=stream)
+        dst = run if step == 0 else chunk
+        lwm_attn_fwd(desc, LWM_OUT_PARTIAL, q, k_chunks[c], v_chunks[c], seg_q, seg_k_chunks[c],
+                     tables[c], m=dst[0], l=dst[1], acc=dst[2], stream=stream)
+        last = step == len(live) - 1
+        if step > 0:
+            lwm_attn_merge_chunk(rows, D, *run, *chunk, finalize=last, out_dtype=odt, o=o,
+                                 lse=lse, stream=stream)
+        elif last:
+            lwm_attn_merge_chunk(rows, D, *run, finalize=True, out_dtype=odt, o=o, lse=lse,
+                                 stream=stream)
+    return o, lse, tables

@@ -1,0 +1,197 @@
+// Host side of the C-ABI declared in include/lwm_attn.h: argument validation, dispatch by
+// dtype and head width, launch on the caller's stream, error mapping.  Holds no state.
+
+#include <algorithm>
+#include <cstdint>
+#include <limits>
+
+#include "common.h"
+
+namespace {
+
+using lwm::TableLayout;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_desc(const lwm_attn_desc* d) {
+  if (d == nullptr) return LWM_ERR_INVALID_ARG;
+  if (d->dtype != LWM_BF16 && d->dtype != LWM_F32) return LWM_ERR_INVALID_ARG;
+  if (d->B <= 0 || d->H <= 0 || d->Sq < 0 || d->Sk < 0 || d->D <= 0) return LWM_ERR_SHAPE;
+  if (d->q_offset < 0 || d->k_offset < 0) return LWM_ERR_SHAPE;
+  if (d->causal != 0 && d->causal != 1) return LWM_ERR_INVALID_ARG;
+  if (!(d->block_q == 16 || d->block_q == 32 || d->block_q == 64)) return LWM_ERR_INVALID_ARG;
+  if (!(d->block_k == 16 || d->block_k == 32 || d->block_k == 64)) return LWM_ERR_INVALID_ARG;
+  // element counts must fit the 64-bit index math and the 32-bit grid dimensions used
+  const int64_t rows_q = int64_t(d->B) * d->H * d->Sq;
+  const int64_t rows_k = int64_t(d->B) * d->H * d->Sk;
+  if (rows_q > (int64_t(1) << 40) || rows_k > (int64_t(1) << 40)) return LWM_ERR_SHAPE;
+  if (d->q_offset > (int64_t(1) << 50) || d->k_offset > (int64_t(1) << 50)) return LWM_ERR_SHAPE;
+  return LWM_OK;
+}
+
+int check_attention_desc(const lwm_attn_desc* d) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (!(d->scale > 0.f) || d->scale == std::numeric_limits<float>::infinity())
+    return LWM_ERR_INVALID_ARG;
+  if (d->block_q != 64 || d->block_k != 64) return LWM_ERR_UNSUPPORTED;
+  if (d->dtype == LWM_BF16 && d->D != 128) return LWM_ERR_UNSUPPORTED;
+  if (d->dtype == LWM_F32 && d->D != 32 && d->D != 64) return LWM_ERR_UNSUPPORTED;
+  // grid: one workgroup per 128-row tile per (b, h) must fit a 32-bit grid
+  const int64_t tiles = int64_t((std::max(d->Sq, d->Sk) + 127) / 128) * d->H * d->B;
+  if (tiles >= (int64_t(1) << 31)) return LWM_ERR_SHAPE;
+  return LWM_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? LWM_OK : LWM_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* lwm_attn_status_string(int status) {
+  switch (status) {
+    case LWM_OK: return "LWM_OK";
+    case LWM_ERR_INVALID_ARG: return "LWM_ERR_INVALID_ARG: null pointer or invalid argument";
+    case LWM_ERR_SHAPE: return "LWM_ERR_SHAPE: inconsistent or out-of-range sizes";
+    case LWM_ERR_ALIGNMENT: return "LWM_ERR_ALIGNMENT: device pointer not 16-byte aligned";
+    case LWM_ERR_UNSUPPORTED: return "LWM_ERR_UNSUPPORTED: dtype / head width / block size not built";
+    case LWM_ERR_WORKSPACE: return "LWM_ERR_WORKSPACE: workspace missing or too small";
+    case LWM_ERR_HIP: return "LWM_ERR_HIP: kernel launch failed";
+    default: return "LWM_ERR_UNKNOWN";
+  }
+}
+
+int lwm_attn_version(void) { return 100; }
+
+size_t lwm_attn_block_table_bytes(const lwm_attn_desc* d) {
+  if (check_desc(d) != LWM_OK) return 0;
+  return lwm::table_layout(*d).total;
+}
+
+int lwm_attn_build_block_table(const lwm_attn_desc* d, const int32_t* seg_q, const int32_t* seg_k,
+                               void* table, void* stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (!table || (d->Sq > 0 && !seg_q) || (d->Sk > 0 && !seg_k)) return LWM_ERR_INVALID_ARG;
+  const void* ptrs[] = {seg_q, seg_k, table};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return LWM_ERR_ALIGNMENT;
+  const TableLayout L = lwm::table_layout(*d);
+  if (int64_t(d->B) * L.nqb * L.nkb >= (int64_t(1) << 39)) return LWM_ERR_SHAPE;
+  return hip_status(lwm::launch_build_table(*d, seg_q, seg_k, table, static_cast<hipStream_t>(stream)));
+}
+
+int lwm_attn_fwd(const lwm_attn_desc* d, int32_t mode, const void* q, const void* k, const void* v,
+                 const int32_t* seg_q, const int32_t* seg_k, const void* table, void* o, float* lse,
+                 float* m, float* l, float* acc, void* stream) {
+  int rc = check_attention_desc(d);
+  if (rc) return rc;
+  if (mode != LWM_OUT_FINAL && mode != LWM_OUT_PARTIAL) return LWM_ERR_INVALID_ARG;
+  if (d->Sq == 0) return LWM_OK;
+  if (!q || !seg_q || !table) return LWM_ERR_INVALID_ARG;
+  if (d->Sk > 0 && (!k || !v || !seg_k)) return LWM_ERR_INVALID_ARG;
+  if (mode == LWM_OUT_FINAL && (!o || !lse)) return LWM_ERR_INVALID_ARG;
+  if (mode == LWM_OUT_PARTIAL && (!m || !l || !acc)) return LWM_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, seg_q, seg_k, table, o, lse, m, l, acc};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return LWM_ERR_ALIGNMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (d->dtype == LWM_BF16)
+    e = lwm::launch_fwd_bf16(*d, mode, q, k, v, seg_q, seg_k, table, o, lse, m, l, acc, s);
+  else
+    e = lwm::launch_fwd_f32(*d, mode, static_cast<const float*>(q), static_cast<const float*>(k),
+                            static_cast<const float*>(v), seg_q, seg_k, table,
+                            static_cast<float*>(o), lse, m, l, acc, s);
+  return hip_status(e);
+}
+
+int lwm_attn_merge_chunk(int64_t rows, int32_t D, float* m, float* l, float* acc, const float* mc,
+                         const float* lc, const float* accc, int32_t finalize, int32_t out_dtype,
+                         void* o, float* lse, void* stream) {
+  if (rows < 0 || D <= 0 || D % 4 != 0 || D > 256) return LWM_ERR_SHAPE;
+  if (rows > (int64_t(1) << 40) / 64) return LWM_ERR_SHAPE;
+  if (finalize != 0 && finalize != 1) return LWM_ERR_INVALID_ARG;
+  if (out_dtype != LWM_BF16 && out_dtype != LWM_F32) return LWM_ERR_INVALID_ARG;
+  const bool any_chunk = mc || lc || accc;
+  const bool all_chunk = mc && lc && accc;
+  if (any_chunk && !all_chunk) return LWM_ERR_INVALID_ARG;
+  if (!all_chunk && !finalize) return LWM_ERR_INVALID_ARG;
+  if (rows == 0) return LWM_OK;
+  if (!m || !l || !acc) return LWM_ERR_INVALID_ARG;
+  if (finalize && (!o || !lse)) return LWM_ERR_INVALID_ARG;
+  const void* ptrs[] = {m, l, acc, mc, lc, accc, o, lse};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return LWM_ERR_ALIGNMENT;
+  return hip_status(lwm::launch_merge(rows, D, m, l, acc, mc, lc, accc, finalize, out_dtype, o,
+                                      lse, static_cast<hipStream_t>(stream)));
+}
+
+size_t lwm_attn_bwd_workspace_bytes(const lwm_attn_desc* d) {
+  if (check_desc(d) != LWM_OK) return 0;
+  return lwm::align256(size_t(d->B) * d->H * d->Sq * sizeof(float));  // Delta
+}
+
+static int bwd_impl(const lwm_attn_desc* d, int phase, const void* q, const void* k,
+                    const void* v, const void* o, const void* dO, const float* lse,
+                    const int32_t* seg_q, const int32_t* seg_k, const void* table, void* dq,
+                    void* dk, void* dv, void* workspace, size_t ws_bytes, void* stream) {
+  int rc = check_attention_desc(d);
+  if (rc) return rc;
+  if (phase < -1 || phase > LWM_BWD_DKV) return LWM_ERR_INVALID_ARG;
+  if (d->Sq == 0 && d->Sk == 0) return LWM_OK;
+  if (!table) return LWM_ERR_INVALID_ARG;
+  if (d->Sq > 0 && (!q || !o || !dO || !lse || !seg_q || !dq)) return LWM_ERR_INVALID_ARG;
+  if (d->Sk > 0 && (!k || !v || !seg_k || !dk || !dv)) return LWM_ERR_INVALID_ARG;
+  const size_t need = lwm_attn_bwd_workspace_bytes(d);
+  if (need > 0 && (!workspace || ws_bytes < need)) return LWM_ERR_WORKSPACE;
+  const void* ptrs[] = {q, k, v, o, dO, lse, seg_q, seg_k, table, dq, dk, dv, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return LWM_ERR_ALIGNMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* delta = static_cast<float*>(workspace);
+  if (d->Sq == 0 || d->Sk == 0) {
+    // no pairs: every gradient is zero (row bytes D*esz are a multiple of 16 for every
+    // supported D)
+    const size_t esz = d->dtype == LWM_BF16 ? 2 : 4;
+    hipError_t e = hipSuccess;
+    if (d->Sq > 0 && (phase < 0 || phase == LWM_BWD_DQ))
+      e = lwm::launch_zero(dq, size_t(d->B) * d->H * d->Sq * d->D * esz, s);
+    if (e == hipSuccess && d->Sk > 0 && (phase < 0 || phase == LWM_BWD_DKV)) {
+      e = lwm::launch_zero(dk, size_t(d->B) * d->H * d->Sk * d->D * esz, s);
+      if (e == hipSuccess) e = lwm::launch_zero(dv, size_t(d->B) * d->H * d->Sk * d->D * esz, s);
+    }
+    return hip_status(e);
+  }
+  hipError_t e;
+  if (d->dtype == LWM_BF16)
+    e = lwm::launch_bwd_bf16(*d, phase, q, k, v, o, dO, lse, seg_q, seg_k, table, dq, dk, dv,
+                             delta, s);
+  else
+    e = lwm::launch_bwd_f32(*d, phase, static_cast<const float*>(q), static_cast<const float*>(k),
+                            static_cast<const float*>(v), static_cast<const float*>(o),
+                            static_cast<const float*>(dO), lse, seg_q, seg_k, table,
+                            static_cast<float*>(dq), static_cast<float*>(dk),
+                            static_cast<float*>(dv), delta, s);
+  return hip_status(e);
+}
+
+int lwm_attn_bwd(const lwm_attn_desc* d, const void* q, const void* k, const void* v,
+                 const void* o, const void* dO, const float* lse, const int32_t* seg_q,
+                 const int32_t* seg_k, const void* table, void* dq, void* dk, void* dv,
+                 void* workspace, size_t ws_bytes, void* stream) {
+  return bwd_impl(d, -1, q, k, v, o, dO, lse, seg_q, seg_k, table, dq, dk, dv, workspace,
+                  ws_bytes, stream);
+}
+
+int lwm_attn_bwd_phase(const lwm_attn_desc* d, int32_t phase, const void* q, const void* k,
+                       const void* v, const void* o, const void* dO, const float* lse,
+                       const int32_t* seg_q, const int32_t* seg_k, const void* table, void* dq,
+                       void* dk, void* dv, void* workspace, size_t ws_bytes, void* stream) {
+  if (phase < 0) return LWM_ERR_INVALID_ARG;
+  return bwd_impl(d, phase, q, k, v, o, dO, lse, seg_q, seg_k, table, dq, dk, dv, workspace,
+                  ws_bytes, stream);
+}
+
+}  // extern "C"

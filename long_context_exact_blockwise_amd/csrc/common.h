@@ -1,0 +1,95 @@
+// Internal declarations shared by the HIP kernels and the host-side C-ABI glue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "lwm_attn.h"
+
+namespace lwm {
+
+// Block-table buffer layout: q_range, k_range, status, then the per-block segment
+// statistics the builder derives them from, each part on a 256-byte boundary.
+struct TableLayout {
+  int32_t nqb, nkb;
+  size_t q_range_off, k_range_off, status_off, q_stats_off, k_stats_off, total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline TableLayout table_layout(const lwm_attn_desc& d) {
+  TableLayout t;
+  t.nqb = (d.Sq + d.block_q - 1) / d.block_q;
+  t.nkb = (d.Sk + d.block_k - 1) / d.block_k;
+  t.q_range_off = 0;
+  t.k_range_off = align256(size_t(d.B) * t.nqb * 2 * sizeof(int32_t));
+  t.status_off = t.k_range_off + align256(size_t(d.B) * t.nkb * 2 * sizeof(int32_t));
+  t.q_stats_off = t.status_off + align256(size_t(d.B) * t.nqb * t.nkb);
+  t.k_stats_off = t.q_stats_off + align256(size_t(d.B) * t.nqb * 4 * sizeof(int32_t));
+  t.total = t.k_stats_off + align256(size_t(d.B) * t.nkb * 4 * sizeof(int32_t));
+  return t;
+}
+
+// Device view of a built table.
+struct TableView {
+  const int32_t* q_range;  // [B][nqb][2]
+  const int32_t* k_range;  // [B][nkb][2]
+  const uint8_t* status;   // [B][nqb][nkb]
+  int32_t nqb, nkb;
+};
+
+inline TableView table_view(const lwm_attn_desc& d, const void* table) {
+  TableLayout L = table_layout(d);
+  const char* base = static_cast<const char*>(table);
+  return TableView{reinterpret_cast<const int32_t*>(base + L.q_range_off),
+                   reinterpret_cast<const int32_t*>(base + L.k_range_off),
+                   reinterpret_cast<const uint8_t*>(base + L.status_off), L.nqb, L.nkb};
+}
+
+// Scalars every attention kernel needs, passed by value.
+struct AttnParams {
+  int32_t B, H, Sq, Sk;
+  int64_t q_offset, k_offset;
+  float scale;
+  int32_t causal;
+};
+
+inline AttnParams attn_params(const lwm_attn_desc& d) {
+  return AttnParams{d.B, d.H, d.Sq, d.Sk, d.q_offset, d.k_offset, d.scale, d.causal};
+}
+
+// ---- launchers (each returns the launch status) ----------------------------------------
+
+// Zero `bytes` (a multiple of 16) at a 16-byte aligned device address.
+hipError_t launch_zero(void* dst, size_t bytes, hipStream_t stream);
+
+hipError_t launch_build_table(const lwm_attn_desc& d, const int32_t* seg_q, const int32_t* seg_k,
+                              void* table, hipStream_t stream);
+
+hipError_t launch_fwd_f32(const lwm_attn_desc& d, int mode, const float* q, const float* k,
+                          const float* v, const int32_t* seg_q, const int32_t* seg_k,
+                          const void* table, float* o, float* lse, float* m, float* l,
+                          float* acc, hipStream_t stream);
+
+// Backward launchers run one phase (LWM_BWD_*) or all of them (phase < 0).
+hipError_t launch_bwd_f32(const lwm_attn_desc& d, int phase, const float* q, const float* k, const float* v,
+                          const float* o, const float* dO, const float* lse,
+                          const int32_t* seg_q, const int32_t* seg_k, const void* table,
+                          float* dq, float* dk, float* dv, float* delta, hipStream_t stream);
+
+hipError_t launch_fwd_bf16(const lwm_attn_desc& d, int mode, const void* q, const void* k,
+                           const void* v, const int32_t* seg_q, const int32_t* seg_k,
+                           const void* table, void* o, float* lse, float* m, float* l,
+                           float* acc, hipStream_t stream);
+
+hipError_t launch_bwd_bf16(const lwm_attn_desc& d, int phase, const void* q, const void* k, const void* v,
+                           const void* o, const void* dO, const float* lse,
+                           const int32_t* seg_q, const int32_t* seg_k, const void* table,
+                           void* dq, void* dk, void* dv, float* delta, hipStream_t stream);
+
+hipError_t launch_merge(int64_t rows, int32_t D, float* m, float* l, float* acc, const float* mc,
+                        const float* lc, const float* accc, int32_t finalize, int32_t out_dtype,
+                        void* o, float* lse, hipStream_t stream);
+
+}  // namespace lwm

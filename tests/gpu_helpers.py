@@ -1,0 +1,57 @@
+"""Helpers shared by the GPU parity tests: device transfer of seeded inputs and read-back
+of results as float64.  Holds no attention arithmetic."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import lwm_inputs as li
+
+# Tolerances stated for this path: O max-abs 1e-2 (bf16 inputs) / 2e-5 (fp32 inputs),
+# LSE max-abs 1e-3; gradients are held to the same max-abs bars as O.
+TOL_O = {"bf16": 1e-2, "f32": 2e-5}
+TOL_LSE = 1e-3
+TOL_GRAD = {"bf16": 1e-2, "f32": 2e-5}
+
+
+def say(*a):
+    """Print and flush, so a log names the case that was running."""
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(arr, dtype_name):
+    """numpy (float32 values or uint16 bf16 bits) -> contiguous CUDA tensor."""
+    import torch
+
+    if dtype_name == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    return t.cuda().contiguous()
+
+
+def seg_dev(seg):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(seg, dtype=np.int32)).cuda().contiguous()
+
+
+def f64(t):
+    """CUDA tensor -> float64 numpy (exact for bf16 and fp32)."""
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def host_f64(arr, dtype_name):
+    return li.bf16_bits_to_f64(arr) if dtype_name == "bf16" else np.asarray(arr, np.float64)
+
+
+def max_abs(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    if a.size == 0:
+        return 0.0
+    both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
+    d = np.where(both_inf, 0.0, np.abs(a - b))
+    return float(np.max(d))

@@ -1,0 +1,157 @@
+"""Host-side checks of the C-ABI library: it loads, exports every entry point that
+include/lwm_attn.h declares, sizes its buffers as documented, and rejects bad arguments
+with the documented status codes before anything reaches a GPU (no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_exact_blockwise_amd as lwm
+from long_context_exact_blockwise_amd import build as lwm_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lwm_attn.h")
+
+OK, INVALID, SHAPE, ALIGN, UNSUP, WS = 0, -1, -2, -3, -4, -5
+FAKE = 1 << 40  # 16-byte aligned fake device address; never dereferenced by these tests
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(lwm.LIB_PATH):
+        lwm_build.build()
+    return lwm.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lwm_attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls_and_size_queries():
+    names = header_functions()
+    for n in ("lwm_attn_fwd", "lwm_attn_bwd", "lwm_attn_merge_chunk", "lwm_attn_build_block_table",
+              "lwm_attn_block_table_bytes", "lwm_attn_bwd_workspace_bytes"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert set(header_functions()) == set(lwm.EXPORTED)
+
+
+def test_library_is_built_for_gfx950_only():
+    data = open(lwm.LIB_PATH, "rb").read()
+    assert b"gfx950" in data
+    for other in (b"gfx942", b"gfx90a", b"gfx1100"):
+        assert b"amdgcn-amd-amdhsa--" + other not in data
+
+
+def desc(**kw):
+    base = dict(B=1, H=2, Sq=256, Sk=256, D=128, dtype=lwm.LWM_BF16)
+    base.update(kw)
+    return lwm.make_desc(base.pop("B"), base.pop("H"), base.pop("Sq"), base.pop("Sk"),
+                         base.pop("D"), base.pop("dtype"), **base)
+
+
+def test_status_strings(lib):
+    for code in (OK, INVALID, SHAPE, ALIGN, UNSUP, WS, -6):
+        s = lib.lwm_attn_status_string(code).decode()
+        assert s.startswith(lwm.STATUS[code])
+    assert lib.lwm_attn_status_string(-99).decode() == "LWM_ERR_UNKNOWN"
+    assert lib.lwm_attn_version() >= 100
+
+
+def test_table_bytes_follow_documented_layout(lib):
+    def al(x):
+        return (x + 255) // 256 * 256
+
+    for (B, Sq, Sk, bq, bk) in [(1, 256, 256, 64, 64), (2, 1000, 333, 32, 16), (1, 131072, 1048576, 64, 64)]:
+        d = desc(B=B, Sq=Sq, Sk=Sk, block_q=bq, block_k=bk)
+        nqb, nkb = -(-Sq // bq), -(-Sk // bk)
+        expect = al(B * nqb * 8) + al(B * nkb * 8) + al(B * nqb * nkb) + al(B * nqb * 16) + al(B * nkb * 16)
+        assert lwm.lwm_attn_block_table_bytes(d) == expect
+    assert lwm.lwm_attn_block_table_bytes(desc(block_q=48)) == 0
+    assert lwm.lwm_attn_bwd_workspace_bytes(desc(B=2, H=3, Sq=100)) == al(2 * 3 * 100 * 4)
+
+
+def call_fwd(lib, d, mode=0, q=FAKE, k=FAKE, v=FAKE, sq=FAKE, sk=FAKE, t=FAKE, o=FAKE, lse=FAKE,
+             m=None, l=None, acc=None):
+    return lib.lwm_attn_fwd(ctypes.byref(d), mode, q, k, v, sq, sk, t, o, lse, m, l, acc, None)
+
+
+def test_fwd_rejects_bad_arguments(lib):
+    assert lib.lwm_attn_fwd(None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                            None, None) == INVALID
+    assert call_fwd(lib, desc(D=96)) == UNSUP
+    assert call_fwd(lib, desc(D=64)) == UNSUP                       # bf16 needs D = 128
+    assert call_fwd(lib, desc(D=128, dtype=lwm.LWM_F32)) == UNSUP   # f32 built for 32, 64
+    assert call_fwd(lib, desc(block_q=32)) == UNSUP
+    assert call_fwd(lib, desc(block_q=40)) == INVALID
+    assert call_fwd(lib, desc(scale=-1.0)) == INVALID
+    assert call_fwd(lib, desc(Sq=-1)) == SHAPE
+    assert call_fwd(lib, desc(q_offset=-5)) == SHAPE
+    assert call_fwd(lib, desc(), mode=7) == INVALID
+    assert call_fwd(lib, desc(), q=None) == INVALID
+    assert call_fwd(lib, desc(), o=None) == INVALID
+    assert call_fwd(lib, desc(), mode=1) == INVALID                 # PARTIAL needs m, l, acc
+    assert call_fwd(lib, desc(), q=FAKE + 8) == ALIGN
+    assert call_fwd(lib, desc(), lse=FAKE + 4) == ALIGN
+    # no query rows: nothing to do, succeeds without touching any pointer
+    assert call_fwd(lib, desc(Sq=0), q=None, k=None, v=None, sq=None, sk=None, t=None, o=None,
+                    lse=None) == OK
+    d = desc()
+    d.causal = 2
+    assert call_fwd(lib, d) == INVALID
+    d = desc()
+    d.dtype = 9
+    assert call_fwd(lib, d) == INVALID
+
+
+def test_table_builder_rejects_bad_arguments(lib):
+    f = lib.lwm_attn_build_block_table
+    assert f(ctypes.byref(desc()), None, FAKE, FAKE, None) == INVALID
+    assert f(ctypes.byref(desc()), FAKE, FAKE, FAKE + 2, None) == ALIGN
+    assert f(ctypes.byref(desc(block_k=128)), FAKE, FAKE, FAKE, None) == INVALID
+    assert f(ctypes.byref(desc(B=0)), FAKE, FAKE, FAKE, None) == SHAPE
+
+
+def test_merge_rejects_bad_arguments(lib):
+    f = lib.lwm_attn_merge_chunk
+    args = lambda **kw: [kw.get(n, FAKE) for n in ("m", "l", "acc", "mc", "lc", "accc")]
+    assert f(10, 130, *args(), 0, 0, None, None, None) == SHAPE       # D % 4
+    assert f(10, 512, *args(), 0, 0, None, None, None) == SHAPE       # D > 256
+    assert f(-1, 128, *args(), 0, 0, None, None, None) == SHAPE
+    assert f(10, 128, *args(), 2, 0, None, None, None) == INVALID     # finalize flag
+    assert f(10, 128, *args(), 0, 5, None, None, None) == INVALID     # out dtype
+    assert f(10, 128, *args(lc=None), 0, 0, None, None, None) == INVALID   # partial chunk
+    assert f(10, 128, *args(mc=None, lc=None, accc=None), 0, 0, None, None, None) == INVALID
+    assert f(10, 128, *args(), 1, 0, None, FAKE, None) == INVALID     # finalize needs o
+    assert f(10, 128, *args(acc=FAKE + 4), 0, 0, None, None, None) == ALIGN
+    assert f(0, 128, *args(), 0, 0, None, None, None) == OK           # no rows
+
+
+def test_bwd_rejects_bad_arguments(lib):
+    f = lib.lwm_attn_bwd
+
+    def call(d, ws=FAKE, ws_bytes=1 << 30, **kw):
+        names = ("q", "k", "v", "o", "do", "lse", "sq", "sk", "t", "dq", "dk", "dv")
+        return f(ctypes.byref(d), *[kw.get(n, FAKE) for n in names], ws, ws_bytes, None)
+
+    assert call(desc(D=64)) == UNSUP
+    assert call(desc(), do=None) == INVALID
+    assert call(desc(), ws=None) == WS
+    assert call(desc(), ws_bytes=16) == WS
+    assert call(desc(), dk=FAKE + 2) == ALIGN
+    assert call(desc(Sq=0, Sk=0)) == OK
+
+
+def test_bwd_phase_rejects_bad_phase(lib):
+    f = lib.lwm_attn_bwd_phase
+    args = [FAKE] * 12
+    assert f(ctypes.byref(desc()), 3, *args, FAKE, 1 << 30, None) == INVALID
+    assert f(ctypes.byref(desc()), -1, *args, FAKE, 1 << 30, None) == INVALID
+    assert f(ctypes.byref(desc(D=64)), 1, *args, FAKE, 1 << 30, None) == UNSUP
