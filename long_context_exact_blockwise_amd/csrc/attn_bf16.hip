@@ -12,6 +12,11 @@
 // workgroup (32 per wave), key tiles of 64 streamed through LDS.  dK/dV: 128 keys per
 // workgroup (32 per wave), query tiles of 64 streamed through LDS.  The table is built with
 // 64 x 64 blocks; a 128-row tile combines two table rows (or columns).
+//
+// Every streamed tile is stored once, row-major and swizzled (mfma_tile.h); operands that
+// run across its rows (V^T, K^T, Q^T, dO^T) are read with the gfx950 transposing LDS read.
+// The next tile's global loads are issued into registers before the current tile is
+// computed and written to LDS after it.
 
 #include <cmath>
 
@@ -23,13 +28,16 @@ namespace {
 
 constexpr int D = 128;
 constexpr int BQ = 128;          // query rows per forward / dQ workgroup
-constexpr int BK = 64;           // keys per streamed tile
+constexpr int BK = 64;           // rows per streamed tile
 constexpr int TB = 64;           // table block size
 constexpr int NT = 256;          // threads per workgroup
-constexpr int RSTR = D + 8;      // row stride (bf16) of row-major [row][d] LDS tiles
-constexpr int TSTR = BK + 8;     // row stride (bf16) of transposed [d][row] LDS tiles
+constexpr int kChunks = BK * D / 8 / NT;  // 16-byte chunks per thread per tile (4)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// The running max moves only when a tile's max exceeds it by more than this (log2 units),
+// so weights stay below 2^kTau and the accumulator is rescaled rarely; l and acc always
+// refer to the max actually used, so the result is exact up to rounding.
+constexpr float kTau = 8.0f;
 
 __device__ __forceinline__ uint8_t combine_status(uint8_t a, uint8_t b) {
   if (a == LWM_TILE_SKIP && b == LWM_TILE_SKIP) return LWM_TILE_SKIP;
@@ -37,27 +45,59 @@ __device__ __forceinline__ uint8_t combine_status(uint8_t a, uint8_t b) {
   return LWM_TILE_PARTIAL;
 }
 
-// Copy a [64 rows][128 d] bf16 tile (rows row0.., zero past `nrows`) from global into a
-// row-major LDS tile, and optionally into a transposed [128 d][64 rows] LDS tile.
-template <bool kTranspose, bool kRowMajor>
-__device__ __forceinline__ void stage_tile(const uint16_t* __restrict__ src, int row0, int nrows,
-                                          uint16_t* rm, uint16_t* tr, int tid) {
-#pragma unroll
-  for (int it = 0; it < (BK * D / 8) / NT; ++it) {
-    const int c = tid + it * NT;
-    const int r = c >> 4, c16 = c & 15;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row0 + r < nrows) v = gload16(src + int64_t(row0 + r) * D + c16 * 8);
-    if (kRowMajor) *reinterpret_cast<uint4*>(rm + r * RSTR + c16 * 8) = v;
-    if (kTranspose) {
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        tr[(c16 * 8 + 2 * e) * TSTR + r] = uint16_t(w[e] & 0xffff);
-        tr[(c16 * 8 + 2 * e + 1) * TSTR + r] = uint16_t(w[e] >> 16);
-      }
-    }
+// Union of two inclusive ranges (an empty range has first > last).
+__device__ __forceinline__ void range_union(const int32_t* a, const int32_t* b, bool has_b, int& lo,
+                                            int& hi) {
+  lo = a[0];
+  hi = a[1];
+  if (has_b && b[1] >= b[0]) {
+    lo = hi >= lo ? min(lo, b[0]) : b[0];
+    hi = max(hi, b[1]);
   }
+}
+
+// Registers holding one 64-row tile in flight between global memory and LDS.
+struct TileRegs {
+  uint4 c[kChunks];
+};
+
+__device__ __forceinline__ void tile_gload(TileRegs& r, const uint16_t* __restrict__ src, int row0,
+                                           int nrows, int tid) {
+#pragma unroll
+  for (int it = 0; it < kChunks; ++it) {
+    const int cidx = tid + it * NT;
+    const int row = cidx >> 4, ch = cidx & 15;
+    r.c[it] = make_uint4(0, 0, 0, 0);
+    if (row0 + row < nrows) r.c[it] = gload16(src + int64_t(row0 + row) * D + ch * 8);
+  }
+}
+
+__device__ __forceinline__ void tile_store(const TileRegs& r, uint16_t* tile, int tid) {
+#pragma unroll
+  for (int it = 0; it < kChunks; ++it) {
+    const int cidx = tid + it * NT;
+    const int row = cidx >> 4, ch = cidx & 15;
+    *reinterpret_cast<uint4*>(tile + tile_off(row, ch * 8)) = r.c[it];
+  }
+}
+
+// First non-SKIP tile at or after kt in [kt, hi] (hi + 1 if none) of a pair of table rows.
+__device__ __forceinline__ int next_live(const uint8_t* s0, const uint8_t* s1, bool has1, int kt,
+                                         int hi) {
+  while (kt <= hi && combine_status(s0[kt], has1 ? s1[kt] : uint8_t(LWM_TILE_SKIP)) == LWM_TILE_SKIP)
+    ++kt;
+  return kt;
+}
+
+// Same over a pair of table columns (stride nkb between rows).
+__device__ __forceinline__ int next_live_col(const uint8_t* base, int64_t nkb, int c0, bool has1,
+                                             int qb, int hi) {
+  while (qb <= hi) {
+    const uint8_t* row = base + qb * nkb;
+    if (combine_status(row[c0], has1 ? row[c0 + 1] : uint8_t(LWM_TILE_SKIP)) != LWM_TILE_SKIP) break;
+    ++qb;
+  }
+  return qb;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -70,8 +110,8 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
                 const int32_t* __restrict__ seg_q, const int32_t* __restrict__ seg_k,
                 uint16_t* __restrict__ O, float* __restrict__ LSE, float* __restrict__ Mo,
                 float* __restrict__ Lo, float* __restrict__ ACC) {
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[BK * RSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * TSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[BK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[BK * D];
   __shared__ int32_t segk_lds[BK];
 
   // Longest rows first: rank 0 is the last query tile; heads are interleaved so that
@@ -87,6 +127,7 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
   const uint16_t* Qh = Q + bh * p.Sq * D;
   const uint16_t* Kh = K + bh * p.Sk * D;
   const uint16_t* Vh = V + bh * p.Sk * D;
+  const int32_t* segk_b = seg_k + int64_t(b) * p.Sk;
 
   const int qrow = qt * BQ + wave * 32 + col;
   const bool qlive = qrow < p.Sq;
@@ -100,17 +141,11 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
   const int32_t sq = qlive ? seg_q[int64_t(b) * p.Sq + qrow] : -1;
   const int64_t qpos = p.q_offset + qrow;
 
-  const int r0 = 2 * qt, r1 = 2 * qt + 1;
-  const bool has_r1 = r1 < t.nqb;
+  const int r0 = 2 * qt;
+  const bool has_r1 = r0 + 1 < t.nqb;
   const int32_t* rg0 = t.q_range + (int64_t(b) * t.nqb + r0) * 2;
-  int lo = rg0[0], hi = rg0[1];
-  if (has_r1) {
-    const int32_t* rg1 = rg0 + 2;
-    if (rg1[1] >= rg1[0]) {
-      lo = hi >= lo ? min(lo, rg1[0]) : rg1[0];
-      hi = max(hi, rg1[1]);
-    }
-  }
+  int lo, hi;
+  range_union(rg0, rg0 + 2, has_r1, lo, hi);
   const uint8_t* st0 = t.status + (int64_t(b) * t.nqb + r0) * t.nkb;
   const uint8_t* st1 = st0 + t.nkb;
 
@@ -120,26 +155,37 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{0};
 
-  for (int kt = lo; kt <= hi; ++kt) {
+  TileRegs kbuf, vbuf;
+  int segbuf = -1;
+  int kt = next_live(st0, st1, has_r1, lo, hi);
+  if (kt <= hi) {
+    tile_gload(kbuf, Kh, kt * BK, p.Sk, tid);
+    tile_gload(vbuf, Vh, kt * BK, p.Sk, tid);
+    if (tid < BK) segbuf = kt * BK + tid < p.Sk ? segk_b[kt * BK + tid] : -1;
+  }
+  while (kt <= hi) {
     const uint8_t st = combine_status(st0[kt], has_r1 ? st1[kt] : uint8_t(LWM_TILE_SKIP));
-    if (st == LWM_TILE_SKIP) continue;
     __syncthreads();
-    stage_tile<false, true>(Kh, kt * BK, p.Sk, k_lds, nullptr, tid);
-    stage_tile<true, false>(Vh, kt * BK, p.Sk, nullptr, vt_lds, tid);
-    if (tid < BK) {
-      const int key = kt * BK + tid;
-      segk_lds[tid] = key < p.Sk ? seg_k[int64_t(b) * p.Sk + key] : -1;
+    tile_store(kbuf, k_lds, tid);
+    tile_store(vbuf, v_lds, tid);
+    if (tid < BK) segk_lds[tid] = segbuf;
+    __syncthreads();
+    const int kn = next_live(st0, st1, has_r1, kt + 1, hi);
+    if (kn <= hi) {
+      tile_gload(kbuf, Kh, kn * BK, p.Sk, tid);
+      tile_gload(vbuf, Vh, kn * BK, p.Sk, tid);
+      if (tid < BK) segbuf = kn * BK + tid < p.Sk ? segk_b[kn * BK + tid] : -1;
     }
-    __syncthreads();
 
-    // S^T = K Q^T for two 32-key blocks
+    // S^T = K Q^T for two 32-key blocks (K rows loaded in kperm order)
     f32x16 sacc[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       sacc[sub] = f32x16{0};
-      const uint16_t* krow = k_lds + (32 * sub + kperm(col)) * RSTR + 8 * hf;
+      const int krow = 32 * sub + kperm(col);
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) sacc[sub] = mfma32(lds_load8(krow + 16 * s), qreg[s], sacc[sub]);
+      for (int s = 0; s < D / 16; ++s)
+        sacc[sub] = mfma32(lds_load8(k_lds + tile_off(krow, 16 * s + 8 * hf)), qreg[s], sacc[sub]);
     }
 
     if (st == LWM_TILE_PARTIAL) {
@@ -160,10 +206,11 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[sub][i]);
-    mx = half_max(mx);
-    const float m_new = fmaxf(m_run, mx * c);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    const float mxc = half_max(mx) * c;
+    const bool upd = mxc > m_run + kTau;  // false while every key so far is masked
+    const float alpha = upd ? fast_exp2(m_run - mxc) : 1.f;
+    if (upd) m_run = mxc;
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float psum = 0.f;
     bf16x8 pb[4];
 #pragma unroll
@@ -173,25 +220,26 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
         float pv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          pv[j] = exp2f(fmaf(sacc[sub][8 * a + j], c, -m_use));
+          pv[j] = fast_exp2(fmaf(sacc[sub][8 * a + j], c, -m_use));
           psum += pv[j];
         }
         pb[2 * sub + a] = to_bf16x8(pv);
       }
     l_run = l_run * alpha + psum;
-    m_run = m_new;
+    if (__ballot(upd) != 0) {
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    }
 
-    // O^T += V^T P^T over four 16-key steps
+    // O^T += V^T P^T over four 16-key steps; V^T read transposed from the row-major tile
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
-        oacc[db] = mfma32(lds_load8(vt_lds + (32 * db + col) * TSTR + 16 * ks + 8 * hf), pb[ks],
-                          oacc[db]);
+        oacc[db] = mfma32(lds_load_tr8(v_lds, 16 * ks, 32 * db, lane), pb[ks], oacc[db]);
+    kt = kn;
   }
 
   const float l_tot = half_sum(l_run);
@@ -254,16 +302,15 @@ __global__ void __launch_bounds__(NT) delta_bf16_kernel(int64_t rows, const uint
 }
 
 // dQ: query-major like the forward.  Per key tile: S^T = K Q^T, dP^T = V dO^T,
-// dS^T = P^T (dP^T - Delta), dQ^T += K^T dS^T.
-__global__ void __launch_bounds__(NT, 2)
+// dS^T = P^T (dP^T - Delta), dQ^T += K^T dS^T (K^T read transposed from the K tile).
+__global__ void __launch_bounds__(NT, 1)
 dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ Q,
                const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
                const float* __restrict__ delta, const int32_t* __restrict__ seg_q,
                const int32_t* __restrict__ seg_k, uint16_t* __restrict__ dQ) {
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[BK * RSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[BK * RSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t kt_lds[D * TSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[BK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[BK * D];
   __shared__ int32_t segk_lds[BK];
 
   const int idx = blockIdx.x;
@@ -275,6 +322,7 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
   const int64_t bh = int64_t(b) * p.H + h;
   const uint16_t* Kh = K + bh * p.Sk * D;
   const uint16_t* Vh = V + bh * p.Sk * D;
+  const int32_t* segk_b = seg_k + int64_t(b) * p.Sk;
 
   const int qrow = qt * BQ + wave * 32 + col;
   const bool qlive = qrow < p.Sq;
@@ -295,17 +343,11 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
   const int32_t sq = qlive ? seg_q[int64_t(b) * p.Sq + qrow] : -1;
   const int64_t qpos = p.q_offset + qrow;
 
-  const int r0 = 2 * qt, r1 = 2 * qt + 1;
-  const bool has_r1 = r1 < t.nqb;
+  const int r0 = 2 * qt;
+  const bool has_r1 = r0 + 1 < t.nqb;
   const int32_t* rg0 = t.q_range + (int64_t(b) * t.nqb + r0) * 2;
-  int lo = rg0[0], hi = rg0[1];
-  if (has_r1) {
-    const int32_t* rg1 = rg0 + 2;
-    if (rg1[1] >= rg1[0]) {
-      lo = hi >= lo ? min(lo, rg1[0]) : rg1[0];
-      hi = max(hi, rg1[1]);
-    }
-  }
+  int lo, hi;
+  range_union(rg0, rg0 + 2, has_r1, lo, hi);
   const uint8_t* st0 = t.status + (int64_t(b) * t.nqb + r0) * t.nkb;
   const uint8_t* st1 = st0 + t.nkb;
   const float c = p.scale * kLog2e;
@@ -314,27 +356,38 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) dqacc[i] = f32x16{0};
 
-  for (int kt = lo; kt <= hi; ++kt) {
+  TileRegs kbuf, vbuf;
+  int segbuf = -1;
+  int kt = next_live(st0, st1, has_r1, lo, hi);
+  if (kt <= hi) {
+    tile_gload(kbuf, Kh, kt * BK, p.Sk, tid);
+    tile_gload(vbuf, Vh, kt * BK, p.Sk, tid);
+    if (tid < BK) segbuf = kt * BK + tid < p.Sk ? segk_b[kt * BK + tid] : -1;
+  }
+  while (kt <= hi) {
     const uint8_t st = combine_status(st0[kt], has_r1 ? st1[kt] : uint8_t(LWM_TILE_SKIP));
-    if (st == LWM_TILE_SKIP) continue;
     __syncthreads();
-    stage_tile<true, true>(Kh, kt * BK, p.Sk, k_lds, kt_lds, tid);
-    stage_tile<false, true>(Vh, kt * BK, p.Sk, v_lds, nullptr, tid);
-    if (tid < BK) {
-      const int key = kt * BK + tid;
-      segk_lds[tid] = key < p.Sk ? seg_k[int64_t(b) * p.Sk + key] : -1;
+    tile_store(kbuf, k_lds, tid);
+    tile_store(vbuf, v_lds, tid);
+    if (tid < BK) segk_lds[tid] = segbuf;
+    __syncthreads();
+    const int kn = next_live(st0, st1, has_r1, kt + 1, hi);
+    if (kn <= hi) {
+      tile_gload(kbuf, Kh, kn * BK, p.Sk, tid);
+      tile_gload(vbuf, Vh, kn * BK, p.Sk, tid);
+      if (tid < BK) segbuf = kn * BK + tid < p.Sk ? segk_b[kn * BK + tid] : -1;
     }
-    __syncthreads();
 
     bf16x8 dsb[4];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       f32x16 sacc = f32x16{0}, pacc = f32x16{0};
-      const int rr = (32 * sub + kperm(col)) * RSTR + 8 * hf;
+      const int krow = 32 * sub + kperm(col);
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
-        sacc = mfma32(lds_load8(k_lds + rr + 16 * s), qreg[s], sacc);
-        pacc = mfma32(lds_load8(v_lds + rr + 16 * s), greg[s], pacc);
+        const int off = tile_off(krow, 16 * s + 8 * hf);
+        sacc = mfma32(lds_load8(k_lds + off), qreg[s], sacc);
+        pacc = mfma32(lds_load8(v_lds + off), greg[s], pacc);
       }
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
@@ -342,7 +395,7 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int i = 8 * a + j;
-          float pr = exp2f(fmaf(sacc[i], c, -lse2));
+          float pr = fast_exp2(fmaf(sacc[i], c, -lse2));
           if (st == LWM_TILE_PARTIAL) {
             const int kl = 32 * sub + slot_index(i, hf);
             const int key = kt * BK + kl;
@@ -359,8 +412,8 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
     for (int ks = 0; ks < BK / 16; ++ks)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
-        dqacc[db] = mfma32(lds_load8(kt_lds + (32 * db + col) * TSTR + 16 * ks + 8 * hf), dsb[ks],
-                           dqacc[db]);
+        dqacc[db] = mfma32(lds_load_tr8(k_lds, 16 * ks, 32 * db, lane), dsb[ks], dqacc[db]);
+    kt = kn;
   }
   if (!qlive) return;
   uint16_t* out = dQ + r64 * D;
@@ -377,8 +430,8 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
 }
 
 // dK, dV: key-major.  Workgroup = 128 keys (32 per wave) held in registers; query tiles of
-// 64 stream through LDS in both layouts.  Per 32-query half: S = Q K^T, dP = dO V^T,
-// P = exp(S - LSE), dS = P (dP - Delta), dV^T += dO^T P, dK^T += Q^T dS.
+// 64 stream through LDS.  Per 32-query half: S = Q K^T, dP = dO V^T, P = exp(S - LSE),
+// dS = P (dP - Delta), dV^T += dO^T P, dK^T += Q^T dS (dO^T, Q^T read transposed).
 __global__ void __launch_bounds__(NT, 1)
 dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__ Q,
                 const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -386,10 +439,8 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
                 const float* __restrict__ delta, const int32_t* __restrict__ seg_q,
                 const int32_t* __restrict__ seg_k, uint16_t* __restrict__ dK,
                 uint16_t* __restrict__ dV) {
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[TB * RSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t g_lds[TB * RSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t qt_lds[D * TSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t gt_lds[D * TSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[TB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t g_lds[TB * D];
   __shared__ __attribute__((aligned(16))) float lse_lds[TB];
   __shared__ __attribute__((aligned(16))) float dl_lds[TB];
   __shared__ int32_t segq_lds[TB];
@@ -403,6 +454,9 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
   const int64_t bh = int64_t(b) * p.H + h;
   const uint16_t* Qh = Q + bh * p.Sq * D;
   const uint16_t* Gh = dO + bh * p.Sq * D;
+  const float* lse_h = LSE + bh * p.Sq;
+  const float* dl_h = delta + bh * p.Sq;
+  const int32_t* segq_b = seg_q + int64_t(b) * p.Sq;
 
   const int key = kt * 128 + wave * 32 + col;
   const bool klive = key < p.Sk;
@@ -421,17 +475,11 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
   const int32_t sk = klive ? seg_k[int64_t(b) * p.Sk + key] : -2;
   const int64_t kpos = p.k_offset + key;
 
-  const int c0 = 2 * kt, c1 = 2 * kt + 1;
-  const bool has_c1 = c1 < t.nkb;
+  const int c0 = 2 * kt;
+  const bool has_c1 = c0 + 1 < t.nkb;
   const int32_t* rg0 = t.k_range + (int64_t(b) * t.nkb + c0) * 2;
-  int lo = rg0[0], hi = rg0[1];
-  if (has_c1) {
-    const int32_t* rg1 = rg0 + 2;
-    if (rg1[1] >= rg1[0]) {
-      lo = hi >= lo ? min(lo, rg1[0]) : rg1[0];
-      hi = max(hi, rg1[1]);
-    }
-  }
+  int lo, hi;
+  range_union(rg0, rg0 + 2, has_c1, lo, hi);
   const uint8_t* stb = t.status + int64_t(b) * t.nqb * t.nkb;
   const float c = p.scale * kLog2e;
 
@@ -442,41 +490,63 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
     dvacc[i] = f32x16{0};
   }
 
-  for (int qb = lo; qb <= hi; ++qb) {
-    const uint8_t* row = stb + int64_t(qb) * t.nkb;
-    const uint8_t st = combine_status(row[c0], has_c1 ? row[c1] : uint8_t(LWM_TILE_SKIP));
-    if (st == LWM_TILE_SKIP) continue;
-    __syncthreads();
-    stage_tile<true, true>(Qh, qb * TB, p.Sq, q_lds, qt_lds, tid);
-    stage_tile<true, true>(Gh, qb * TB, p.Sq, g_lds, gt_lds, tid);
+  TileRegs qbuf, gbuf;
+  float lsebuf = 0.f, dlbuf = 0.f;
+  int segbuf = -1;
+  auto gload_all = [&](int qb) {
+    tile_gload(qbuf, Qh, qb * TB, p.Sq, tid);
+    tile_gload(gbuf, Gh, qb * TB, p.Sq, tid);
     if (tid < TB) {
       const int r = qb * TB + tid;
       const bool ok = r < p.Sq;
-      lse_lds[tid] = ok ? LSE[bh * p.Sq + r] * kLog2e : 0.f;
-      dl_lds[tid] = ok ? delta[bh * p.Sq + r] : 0.f;
-      segq_lds[tid] = ok ? seg_q[int64_t(b) * p.Sq + r] : -1;
+      lsebuf = ok ? lse_h[r] * kLog2e : 0.f;
+      dlbuf = ok ? dl_h[r] : 0.f;
+      segbuf = ok ? segq_b[r] : -1;
+    }
+  };
+  int qb = next_live_col(stb, t.nkb, c0, has_c1, lo, hi);
+  if (qb <= hi) gload_all(qb);
+  while (qb <= hi) {
+    const uint8_t* row = stb + int64_t(qb) * t.nkb;
+    const uint8_t st = combine_status(row[c0], has_c1 ? row[c0 + 1] : uint8_t(LWM_TILE_SKIP));
+    __syncthreads();
+    tile_store(qbuf, q_lds, tid);
+    tile_store(gbuf, g_lds, tid);
+    if (tid < TB) {
+      lse_lds[tid] = lsebuf;
+      dl_lds[tid] = dlbuf;
+      segq_lds[tid] = segbuf;
     }
     __syncthreads();
+    const int qn = next_live_col(stb, t.nkb, c0, has_c1, qb + 1, hi);
+    if (qn <= hi) gload_all(qn);
 
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       f32x16 sacc = f32x16{0}, pacc = f32x16{0};
-      const int rr = (32 * sub + kperm(col)) * RSTR + 8 * hf;
+      const int qrow = 32 * sub + kperm(col);
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
-        sacc = mfma32(lds_load8(q_lds + rr + 16 * s), kreg[s], sacc);
-        pacc = mfma32(lds_load8(g_lds + rr + 16 * s), vreg[s], pacc);
+        const int off = tile_off(qrow, 16 * s + 8 * hf);
+        sacc = mfma32(lds_load8(q_lds + off), kreg[s], sacc);
+        pacc = mfma32(lds_load8(g_lds + off), vreg[s], pacc);
       }
       bf16x8 pb[2], dsb[2];
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         const int qbase = 32 * sub + 16 * a + 8 * hf;  // 8 consecutive local query rows
+        const float4 l0 = *reinterpret_cast<const float4*>(lse_lds + qbase);
+        const float4 l1 = *reinterpret_cast<const float4*>(lse_lds + qbase + 4);
+        const float4 d0 = *reinterpret_cast<const float4*>(dl_lds + qbase);
+        const float4 d1 = *reinterpret_cast<const float4*>(dl_lds + qbase + 4);
+        const float lsev[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+        const float dlv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
         float pv[8], ds[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int i = 8 * a + j;
           const int ql = qbase + j;
-          float pr = exp2f(fmaf(sacc[i], c, -lse_lds[ql]));
+          float pr = fast_exp2(fmaf(sacc[i], c, -lsev[j]));
           if (st == LWM_TILE_PARTIAL) {
             const int qr = qb * TB + ql;
             const bool vis = klive && qr < p.Sq && segq_lds[ql] >= 0 && segq_lds[ql] == sk &&
@@ -484,7 +554,7 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
             if (!vis) pr = 0.f;
           }
           pv[j] = pr;
-          ds[j] = pr * (pacc[i] - dl_lds[ql]);
+          ds[j] = pr * (pacc[i] - dlv[j]);
         }
         pb[a] = to_bf16x8(pv);
         dsb[a] = to_bf16x8(ds);
@@ -494,12 +564,12 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
         const int ks = 2 * sub + a;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const int tr = (32 * db + col) * TSTR + 16 * ks + 8 * hf;
-          dvacc[db] = mfma32(lds_load8(gt_lds + tr), pb[a], dvacc[db]);
-          dkacc[db] = mfma32(lds_load8(qt_lds + tr), dsb[a], dkacc[db]);
+          dvacc[db] = mfma32(lds_load_tr8(g_lds, 16 * ks, 32 * db, lane), pb[a], dvacc[db]);
+          dkacc[db] = mfma32(lds_load_tr8(q_lds, 16 * ks, 32 * db, lane), dsb[a], dkacc[db]);
         }
       }
     }
+    qb = qn;
   }
   if (!klive) return;
   uint16_t* ko = dK + k64 * D;
@@ -536,8 +606,8 @@ hipError_t launch_fwd_bf16(const lwm_attn_desc& d, int mode, const void* q, cons
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_bf16(const lwm_attn_desc& d, int phase, const void* q, const void* k, const void* v,
-                           const void* o, const void* dO, const float* lse,
+hipError_t launch_bwd_bf16(const lwm_attn_desc& d, int phase, const void* q, const void* k,
+                           const void* v, const void* o, const void* dO, const float* lse,
                            const int32_t* seg_q, const int32_t* seg_k, const void* table,
                            void* dq, void* dk, void* dv, float* delta, hipStream_t stream) {
   const TableView t = table_view(d, table);

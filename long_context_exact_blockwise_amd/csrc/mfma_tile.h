@@ -20,6 +20,8 @@
 namespace lwm {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -62,6 +64,41 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float* x) {
 __device__ __forceinline__ bf16x8 lds_load8(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
+
+// ---- LDS tiles of 128-wide bf16 rows ------------------------------------------------------
+//
+// A tile holds rows of 128 bf16 (256 bytes, 16 chunks of 16 bytes).  Chunk c of row r is
+// stored at chunk c ^ tile_swz(r), which keeps three access patterns free of bank conflicts:
+//   - 16-byte row reads by 16 lanes on 16 distinct rows of an aligned 16-row group (MFMA
+//     operands taken along the row),
+//   - transposed reads (ds_read_b64_tr_b16) of 4 consecutive rows x 32 columns,
+//   - 16-byte writes of one row by 16 lanes while staging from global memory.
+__device__ __forceinline__ int tile_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+__device__ __forceinline__ int tile_off(int row, int col) {
+  return row * 128 + ((((col >> 3) ^ tile_swz(row))) << 3) + (col & 7);
+}
+
+// MFMA operand read across rows of a tile with ds_read_b64_tr_b16: lane l receives
+// T[r0 + 8h + j][c0 + l%32] for j = 0..7 (h = l/32), i.e. the A/B operand of an MFMA whose
+// M (or N) index is the tile column and whose k index is the tile row.  Within each group
+// of 16 lanes, lane 4j+p supplies the address of row j, columns 4p..4p+3 of its group's
+// 4 x 16 block, and the instruction hands lane i column i of rows 0..3.  r0 must be a
+// multiple of 8 and c0 a multiple of 32.
+__device__ __forceinline__ bf16x8 lds_load_tr8(const uint16_t* tile, int r0, int c0, int lane) {
+  const int g = lane >> 4, r = lane & 15;
+  const int row = r0 + 8 * (g >> 1) + (r >> 2);
+  const int col = c0 + 16 * (g & 1) + 4 * (r & 3);
+  typedef i16x4 __attribute__((address_space(3))) * lds_i16x4_ptr;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(tile + tile_off(row, col)));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(tile + tile_off(row + 4, col)));
+  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// exp2 straight from the hardware unit (v_exp_f32, about 1 ulp) without the library's
+// denormal range fix-up: results below 2^-126 flush to zero, which softmax weights afford.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ uint4 gload16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
