@@ -18,6 +18,7 @@
 // The next tile's global loads are issued into registers before the current tile is
 // computed and written to LDS after it.
 
+#include <climits>
 #include <cmath>
 
 #include "common.h"
@@ -39,6 +40,10 @@ constexpr float kLn2 = 0.6931471805599453f;
 // refer to the max actually used, so the result is exact up to rounding.
 constexpr float kTau = 8.0f;
 
+// Values read from the block table are the same on every lane; say so, so that addresses
+// and buffer resources built from them stay in scalar registers.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 __device__ __forceinline__ uint8_t combine_status(uint8_t a, uint8_t b) {
   if (a == LWM_TILE_SKIP && b == LWM_TILE_SKIP) return LWM_TILE_SKIP;
   if (a == LWM_TILE_FULL && b == LWM_TILE_FULL) return LWM_TILE_FULL;
@@ -48,11 +53,14 @@ __device__ __forceinline__ uint8_t combine_status(uint8_t a, uint8_t b) {
 // Union of two inclusive ranges (an empty range has first > last).
 __device__ __forceinline__ void range_union(const int32_t* a, const int32_t* b, bool has_b, int& lo,
                                             int& hi) {
-  lo = a[0];
-  hi = a[1];
-  if (has_b && b[1] >= b[0]) {
-    lo = hi >= lo ? min(lo, b[0]) : b[0];
-    hi = max(hi, b[1]);
+  lo = uniform(a[0]);
+  hi = uniform(a[1]);
+  if (has_b) {
+    const int blo = uniform(b[0]), bhi = uniform(b[1]);
+    if (bhi >= blo) {
+      lo = hi >= lo ? min(lo, blo) : blo;
+      hi = max(hi, bhi);
+    }
   }
 }
 
@@ -61,15 +69,28 @@ struct TileRegs {
   uint4 c[kChunks];
 };
 
+// Buffer resource over `rows` rows of 128 bf16 starting at `base`; loads past the end
+// return zero (hardware range check), so tails need no branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int rows, int row_bytes) {
+  const int bytes = __builtin_amdgcn_readfirstlane(max(rows, 0) * row_bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
 __device__ __forceinline__ void tile_gload(TileRegs& r, const uint16_t* __restrict__ src, int row0,
                                            int nrows, int tid) {
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(src + int64_t(row0) * D, min(nrows - row0, BK), D * 2);
 #pragma unroll
   for (int it = 0; it < kChunks; ++it) {
     const int cidx = tid + it * NT;
-    const int row = cidx >> 4, ch = cidx & 15;
-    r.c[it] = make_uint4(0, 0, 0, 0);
-    if (row0 + row < nrows) r.c[it] = gload16(src + int64_t(row0 + row) * D + ch * 8);
+    r.c[it] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, cidx * 16, 0, 0));
   }
+}
+
+// One 32-bit value per thread (tid < BK) of a per-row vector starting at row0; 0 past the end.
+__device__ __forceinline__ uint32_t row_gload32(const void* src, int row0, int nrows, int tid) {
+  const __amdgpu_buffer_rsrc_t rs =
+      rows_rsrc(static_cast<const char*>(src) + int64_t(row0) * 4, min(nrows - row0, BK), 4);
+  return __builtin_amdgcn_raw_buffer_load_b32(rs, tid * 4, 0, 0);
 }
 
 __device__ __forceinline__ void tile_store(const TileRegs& r, uint16_t* tile, int tid) {
@@ -81,12 +102,27 @@ __device__ __forceinline__ void tile_store(const TileRegs& r, uint16_t* tile, in
   }
 }
 
+// Position difference q_offset - k_offset clamped into int32: with it, key j is causally
+// visible from query row i iff j - i <= dpos (|j - i| < 2^31 always holds).
+__device__ __forceinline__ int clamp_dpos(int64_t q_offset, int64_t k_offset) {
+  const int64_t d = q_offset - k_offset;
+  return int(d > INT32_MAX ? INT32_MAX : (d < INT32_MIN + 1 ? INT32_MIN + 1 : d));
+}
+
+// Eight consecutive int32 from LDS (16-byte aligned).
+__device__ __forceinline__ void lds_load_i8(const int32_t* p, int* v) {
+  const int4 a = *reinterpret_cast<const int4*>(p);
+  const int4 b = *reinterpret_cast<const int4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
 // First non-SKIP tile at or after kt in [kt, hi] (hi + 1 if none) of a pair of table rows.
 __device__ __forceinline__ int next_live(const uint8_t* s0, const uint8_t* s1, bool has1, int kt,
                                          int hi) {
   while (kt <= hi && combine_status(s0[kt], has1 ? s1[kt] : uint8_t(LWM_TILE_SKIP)) == LWM_TILE_SKIP)
     ++kt;
-  return kt;
+  return uniform(kt);
 }
 
 // Same over a pair of table columns (stride nkb between rows).
@@ -97,7 +133,7 @@ __device__ __forceinline__ int next_live_col(const uint8_t* base, int64_t nkb, i
     if (combine_status(row[c0], has1 ? row[c0 + 1] : uint8_t(LWM_TILE_SKIP)) != LWM_TILE_SKIP) break;
     ++qb;
   }
-  return qb;
+  return uniform(qb);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -139,7 +175,7 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
     qreg[s] = *reinterpret_cast<bf16x8*>(&v);
   }
   const int32_t sq = qlive ? seg_q[int64_t(b) * p.Sq + qrow] : -1;
-  const int64_t qpos = p.q_offset + qrow;
+  const int dpos = clamp_dpos(p.q_offset, p.k_offset);
 
   const int r0 = 2 * qt;
   const bool has_r1 = r0 + 1 < t.nqb;
@@ -161,10 +197,10 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
   if (kt <= hi) {
     tile_gload(kbuf, Kh, kt * BK, p.Sk, tid);
     tile_gload(vbuf, Vh, kt * BK, p.Sk, tid);
-    if (tid < BK) segbuf = kt * BK + tid < p.Sk ? segk_b[kt * BK + tid] : -1;
+    if (tid < BK) segbuf = int(row_gload32(segk_b, kt * BK, p.Sk, tid));
   }
   while (kt <= hi) {
-    const uint8_t st = combine_status(st0[kt], has_r1 ? st1[kt] : uint8_t(LWM_TILE_SKIP));
+    const int st = uniform(combine_status(st0[kt], has_r1 ? st1[kt] : uint8_t(LWM_TILE_SKIP)));
     __syncthreads();
     tile_store(kbuf, k_lds, tid);
     tile_store(vbuf, v_lds, tid);
@@ -174,7 +210,7 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
     if (kn <= hi) {
       tile_gload(kbuf, Kh, kn * BK, p.Sk, tid);
       tile_gload(vbuf, Vh, kn * BK, p.Sk, tid);
-      if (tid < BK) segbuf = kn * BK + tid < p.Sk ? segk_b[kn * BK + tid] : -1;
+      if (tid < BK) segbuf = int(row_gload32(segk_b, kn * BK, p.Sk, tid));
     }
 
     // S^T = K Q^T for two 32-key blocks (K rows loaded in kperm order)
@@ -189,15 +225,21 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
     }
 
     if (st == LWM_TILE_PARTIAL) {
+      // branch-free visibility; rows past Sq carry sq = -1 and see nothing
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kl = 32 * sub + slot_index(i, hf);
-          const int key = kt * BK + kl;
-          const bool vis = qlive && key < p.Sk && sq >= 0 && sq == segk_lds[kl] &&
-                           (!p.causal || p.k_offset + key <= qpos);
-          if (!vis) sacc[sub][i] = -INFINITY;
+        for (int a = 0; a < 2; ++a) {
+          const int kl0 = 32 * sub + 16 * a + 8 * hf;
+          int sk8[8];
+          lds_load_i8(segk_lds + kl0, sk8);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int key = kt * BK + kl0 + j;
+            const bool vis = (key < p.Sk) & (sk8[j] == sq) & (sq >= 0) &
+                             ((p.causal == 0) | (key - qrow <= dpos));
+            sacc[sub][8 * a + j] = vis ? sacc[sub][8 * a + j] : -INFINITY;
+          }
         }
     }
 
@@ -303,7 +345,7 @@ __global__ void __launch_bounds__(NT) delta_bf16_kernel(int64_t rows, const uint
 
 // dQ: query-major like the forward.  Per key tile: S^T = K Q^T, dP^T = V dO^T,
 // dS^T = P^T (dP^T - Delta), dQ^T += K^T dS^T (K^T read transposed from the K tile).
-__global__ void __launch_bounds__(NT, 1)
+__global__ void __launch_bounds__(NT, 2)
 dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ Q,
                const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
@@ -341,7 +383,7 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
   const float lse2 = qlive ? LSE[r64] * kLog2e : 0.f;
   const float dl = qlive ? delta[r64] : 0.f;
   const int32_t sq = qlive ? seg_q[int64_t(b) * p.Sq + qrow] : -1;
-  const int64_t qpos = p.q_offset + qrow;
+  const int dpos = clamp_dpos(p.q_offset, p.k_offset);
 
   const int r0 = 2 * qt;
   const bool has_r1 = r0 + 1 < t.nqb;
@@ -362,10 +404,10 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
   if (kt <= hi) {
     tile_gload(kbuf, Kh, kt * BK, p.Sk, tid);
     tile_gload(vbuf, Vh, kt * BK, p.Sk, tid);
-    if (tid < BK) segbuf = kt * BK + tid < p.Sk ? segk_b[kt * BK + tid] : -1;
+    if (tid < BK) segbuf = int(row_gload32(segk_b, kt * BK, p.Sk, tid));
   }
   while (kt <= hi) {
-    const uint8_t st = combine_status(st0[kt], has_r1 ? st1[kt] : uint8_t(LWM_TILE_SKIP));
+    const int st = uniform(combine_status(st0[kt], has_r1 ? st1[kt] : uint8_t(LWM_TILE_SKIP)));
     __syncthreads();
     tile_store(kbuf, k_lds, tid);
     tile_store(vbuf, v_lds, tid);
@@ -375,7 +417,7 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
     if (kn <= hi) {
       tile_gload(kbuf, Kh, kn * BK, p.Sk, tid);
       tile_gload(vbuf, Vh, kn * BK, p.Sk, tid);
-      if (tid < BK) segbuf = kn * BK + tid < p.Sk ? segk_b[kn * BK + tid] : -1;
+      if (tid < BK) segbuf = int(row_gload32(segk_b, kn * BK, p.Sk, tid));
     }
 
     bf16x8 dsb[4];
@@ -392,16 +434,18 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         float ds[8];
+        const int kl0 = 32 * sub + 16 * a + 8 * hf;
+        int sk8[8];
+        if (st == LWM_TILE_PARTIAL) lds_load_i8(segk_lds + kl0, sk8);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int i = 8 * a + j;
           float pr = fast_exp2(fmaf(sacc[i], c, -lse2));
           if (st == LWM_TILE_PARTIAL) {
-            const int kl = 32 * sub + slot_index(i, hf);
-            const int key = kt * BK + kl;
-            const bool vis = qlive && key < p.Sk && sq >= 0 && sq == segk_lds[kl] &&
-                             (!p.causal || p.k_offset + key <= qpos);
-            if (!vis) pr = 0.f;
+            const int key = kt * BK + kl0 + j;
+            const bool vis = (key < p.Sk) & (sk8[j] == sq) & (sq >= 0) &
+                             ((p.causal == 0) | (key - qrow <= dpos));
+            pr = vis ? pr : 0.f;
           }
           ds[j] = pr * (pacc[i] - dl);
         }
@@ -473,7 +517,7 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
     vreg[s] = *reinterpret_cast<bf16x8*>(&v);
   }
   const int32_t sk = klive ? seg_k[int64_t(b) * p.Sk + key] : -2;
-  const int64_t kpos = p.k_offset + key;
+  const int dpos = clamp_dpos(p.q_offset, p.k_offset);
 
   const int c0 = 2 * kt;
   const bool has_c1 = c0 + 1 < t.nkb;
@@ -497,18 +541,16 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
     tile_gload(qbuf, Qh, qb * TB, p.Sq, tid);
     tile_gload(gbuf, Gh, qb * TB, p.Sq, tid);
     if (tid < TB) {
-      const int r = qb * TB + tid;
-      const bool ok = r < p.Sq;
-      lsebuf = ok ? lse_h[r] * kLog2e : 0.f;
-      dlbuf = ok ? dl_h[r] : 0.f;
-      segbuf = ok ? segq_b[r] : -1;
+      lsebuf = __uint_as_float(row_gload32(lse_h, qb * TB, p.Sq, tid)) * kLog2e;
+      dlbuf = __uint_as_float(row_gload32(dl_h, qb * TB, p.Sq, tid));
+      segbuf = int(row_gload32(segq_b, qb * TB, p.Sq, tid));
     }
   };
   int qb = next_live_col(stb, t.nkb, c0, has_c1, lo, hi);
   if (qb <= hi) gload_all(qb);
   while (qb <= hi) {
     const uint8_t* row = stb + int64_t(qb) * t.nkb;
-    const uint8_t st = combine_status(row[c0], has_c1 ? row[c0 + 1] : uint8_t(LWM_TILE_SKIP));
+    const int st = uniform(combine_status(row[c0], has_c1 ? row[c0 + 1] : uint8_t(LWM_TILE_SKIP)));
     __syncthreads();
     tile_store(qbuf, q_lds, tid);
     tile_store(gbuf, g_lds, tid);
@@ -542,16 +584,18 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
         const float lsev[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
         const float dlv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
         float pv[8], ds[8];
+        int sq8[8];
+        if (st == LWM_TILE_PARTIAL) lds_load_i8(segq_lds + qbase, sq8);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int i = 8 * a + j;
-          const int ql = qbase + j;
           float pr = fast_exp2(fmaf(sacc[i], c, -lsev[j]));
           if (st == LWM_TILE_PARTIAL) {
-            const int qr = qb * TB + ql;
-            const bool vis = klive && qr < p.Sq && segq_lds[ql] >= 0 && segq_lds[ql] == sk &&
-                             (!p.causal || kpos <= p.q_offset + qr);
-            if (!vis) pr = 0.f;
+            // keys past Sk carry sk = -2 and rows past Sq fail qr < Sq
+            const int qr = qb * TB + qbase + j;
+            const bool vis = (qr < p.Sq) & (sq8[j] == sk) & (sk >= 0) &
+                             ((p.causal == 0) | (key - qr <= dpos));
+            pr = vis ? pr : 0.f;
           }
           pv[j] = pr;
           ds[j] = pr * (pacc[i] - dlv[j]);
