@@ -130,7 +130,8 @@ int lwm_attn_merge_chunk(int64_t rows, int32_t D, float* m, float* l, float* acc
 
 size_t lwm_attn_bwd_workspace_bytes(const lwm_attn_desc* d) {
   if (check_desc(d) != LWM_OK) return 0;
-  return lwm::align256(size_t(d->B) * d->H * d->Sq * sizeof(float));  // Delta
+  // Delta and LSE * log2(e), one float32 per query row each
+  return 2 * lwm::align256(size_t(d->B) * d->H * d->Sq * sizeof(float));
 }
 
 static int bwd_impl(const lwm_attn_desc* d, int phase, const void* q, const void* k,

@@ -13,10 +13,13 @@
 // workgroup (32 per wave), query tiles of 64 streamed through LDS.  The table is built with
 // 64 x 64 blocks; a 128-row tile combines two table rows (or columns).
 //
-// Every streamed tile is stored once, row-major and swizzled (mfma_tile.h); operands that
-// run across its rows (V^T, K^T, Q^T, dO^T) are read with the gfx950 transposing LDS read.
-// The next tile's global loads are issued into registers before the current tile is
-// computed and written to LDS after it.
+// Streaming: tiles are double-buffered in LDS and filled by the buffer unit directly
+// (buffer_load ... lds), so no registers hold tile data in flight; the loads for tile j+1
+// are issued right after the barrier that opens tile j, and one barrier per tile both
+// publishes tile j+1 and retires the buffer tile j-1 used.  The loop body is instantiated
+// once per buffer half so every LDS address is a register plus a constant offset.  Each tile is stored once,
+// row-major and swizzled (mfma_tile.h); operands that run across its rows (V^T, K^T, Q^T,
+// dO^T) are read with the gfx950 transposing LDS read.
 
 #include <climits>
 #include <cmath>
@@ -32,13 +35,15 @@ constexpr int BQ = 128;          // query rows per forward / dQ workgroup
 constexpr int BK = 64;           // rows per streamed tile
 constexpr int TB = 64;           // table block size
 constexpr int NT = 256;          // threads per workgroup
-constexpr int kChunks = BK * D / 8 / NT;  // 16-byte chunks per thread per tile (4)
+constexpr int kTileElems = BK * D;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // The running max moves only when a tile's max exceeds it by more than this (log2 units),
 // so weights stay below 2^kTau and the accumulator is rescaled rarely; l and acc always
 // refer to the max actually used, so the result is exact up to rounding.
 constexpr float kTau = 8.0f;
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // Values read from the block table are the same on every lane; say so, so that addresses
 // and buffer resources built from them stay in scalar registers.
@@ -64,59 +69,6 @@ __device__ __forceinline__ void range_union(const int32_t* a, const int32_t* b, 
   }
 }
 
-// Registers holding one 64-row tile in flight between global memory and LDS.
-struct TileRegs {
-  uint4 c[kChunks];
-};
-
-// Buffer resource over `rows` rows of 128 bf16 starting at `base`; loads past the end
-// return zero (hardware range check), so tails need no branches.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int rows, int row_bytes) {
-  const int bytes = __builtin_amdgcn_readfirstlane(max(rows, 0) * row_bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-
-__device__ __forceinline__ void tile_gload(TileRegs& r, const uint16_t* __restrict__ src, int row0,
-                                           int nrows, int tid) {
-  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(src + int64_t(row0) * D, min(nrows - row0, BK), D * 2);
-#pragma unroll
-  for (int it = 0; it < kChunks; ++it) {
-    const int cidx = tid + it * NT;
-    r.c[it] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, cidx * 16, 0, 0));
-  }
-}
-
-// One 32-bit value per thread (tid < BK) of a per-row vector starting at row0; 0 past the end.
-__device__ __forceinline__ uint32_t row_gload32(const void* src, int row0, int nrows, int tid) {
-  const __amdgpu_buffer_rsrc_t rs =
-      rows_rsrc(static_cast<const char*>(src) + int64_t(row0) * 4, min(nrows - row0, BK), 4);
-  return __builtin_amdgcn_raw_buffer_load_b32(rs, tid * 4, 0, 0);
-}
-
-__device__ __forceinline__ void tile_store(const TileRegs& r, uint16_t* tile, int tid) {
-#pragma unroll
-  for (int it = 0; it < kChunks; ++it) {
-    const int cidx = tid + it * NT;
-    const int row = cidx >> 4, ch = cidx & 15;
-    *reinterpret_cast<uint4*>(tile + tile_off(row, ch * 8)) = r.c[it];
-  }
-}
-
-// Position difference q_offset - k_offset clamped into int32: with it, key j is causally
-// visible from query row i iff j - i <= dpos (|j - i| < 2^31 always holds).
-__device__ __forceinline__ int clamp_dpos(int64_t q_offset, int64_t k_offset) {
-  const int64_t d = q_offset - k_offset;
-  return int(d > INT32_MAX ? INT32_MAX : (d < INT32_MIN + 1 ? INT32_MIN + 1 : d));
-}
-
-// Eight consecutive int32 from LDS (16-byte aligned).
-__device__ __forceinline__ void lds_load_i8(const int32_t* p, int* v) {
-  const int4 a = *reinterpret_cast<const int4*>(p);
-  const int4 b = *reinterpret_cast<const int4*>(p + 4);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-
 // First non-SKIP tile at or after kt in [kt, hi] (hi + 1 if none) of a pair of table rows.
 __device__ __forceinline__ int next_live(const uint8_t* s0, const uint8_t* s1, bool has1, int kt,
                                          int hi) {
@@ -136,6 +88,88 @@ __device__ __forceinline__ int next_live_col(const uint8_t* base, int64_t nkb, i
   return uniform(qb);
 }
 
+// Position difference q_offset - k_offset clamped into int32: with it, key j is causally
+// visible from query row i iff j - i <= dpos (|j - i| < 2^31 always holds).
+__device__ __forceinline__ int clamp_dpos(int64_t q_offset, int64_t k_offset) {
+  const int64_t d = q_offset - k_offset;
+  return int(d > INT32_MAX ? INT32_MAX : (d < INT32_MIN + 1 ? INT32_MIN + 1 : d));
+}
+
+// Eight consecutive int32 / float from LDS (16-byte aligned).
+__device__ __forceinline__ void lds_load_i8(const int32_t* p, int* v) {
+  const int4 a = *reinterpret_cast<const int4*>(p);
+  const int4 b = *reinterpret_cast<const int4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void lds_load_f8(const float* p, float* v) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource (V#) over `bytes` bytes at `base`: raw addressing, no stride; loads past
+// the end return zero (hardware range check), so tails need no branches.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{__builtin_amdgcn_readfirstlane(int(uint32_t(a))),
+               __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32) & 0xffff)),
+               __builtin_amdgcn_readfirstlane(max(bytes, 0)), 0x00020000};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((lds_ptr)(p)));
+}
+
+// Asynchronous copy global -> LDS by the buffer unit: every lane fetches `bytes` (16 or 4)
+// at rsrc + voff and the unit writes them to LDS at lds_base + lane * bytes.  Issued from
+// inline assembly so that the compiler does not serialise later LDS reads of other buffers
+// behind it; callers wait (wait_vmem) and synchronise before reading the destination.  It
+// has no register results, so nothing the compiler allocates is written after issue.
+__device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const i32x4& rsrc, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// Issue the loads of one 64-row tile (rows row0.. of a [nrows][128] bf16 tensor) straight
+// into a swizzled LDS tile.  Each wave moves 4 blocks of 4 rows (1 KiB each); the buffer
+// unit writes lane l's 16 bytes to block + 16 l, so lane l fetches the logical chunk that
+// belongs at physical chunk l % 16 of its row.  Rows past nrows arrive as zeros.
+__device__ __forceinline__ void tile_async_load(uint16_t* tile, const uint16_t* __restrict__ src,
+                                                int row0, int nrows, int wave, int lane) {
+  const i32x4 rs = make_rsrc(src + int64_t(row0) * D, min(nrows - row0, BK) * D * 2);
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(tile));
+#pragma unroll
+  for (int it = 0; it < BK / 16; ++it) {
+    const int blk = it * 4 + wave;
+    const int row = 4 * blk + (lane >> 4);
+    const uint32_t voff = row * (D * 2) + (((lane & 15) ^ tile_swz(row)) << 4);
+    dma16(rs, __builtin_amdgcn_readfirstlane(base + blk * 1024), voff);
+  }
+}
+
+// Issue the load of 64 consecutive 32-bit values (rows row0.. of a per-row vector) into LDS;
+// called by one whole wave.  Values past nrows arrive as zeros.
+__device__ __forceinline__ void vec_async_load(void* dst, const void* src, int row0, int nrows,
+                                               int lane) {
+  const i32x4 rs = make_rsrc(static_cast<const char*>(src) + int64_t(row0) * 4, min(nrows - row0, BK) * 4);
+  dma4(rs, __builtin_amdgcn_readfirstlane(lds_addr(dst)), lane * 4);
+}
+
+// Wait until this wave's outstanding vector-memory loads (including loads into LDS) are done.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // ---------------------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------------------
@@ -146,9 +180,10 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
                 const int32_t* __restrict__ seg_q, const int32_t* __restrict__ seg_k,
                 uint16_t* __restrict__ O, float* __restrict__ LSE, float* __restrict__ Mo,
                 float* __restrict__ Lo, float* __restrict__ ACC) {
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[BK * D];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[BK * D];
-  __shared__ int32_t segk_lds[BK];
+  // double buffers: half 0 and half 1 of each array
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2 * kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2 * kTileElems];
+  __shared__ __attribute__((aligned(16))) int32_t segk_lds[2 * BK];
 
   // Longest rows first: rank 0 is the last query tile; heads are interleaved so that
   // consecutive workgroups (spread over the XCDs) share a tile rank.
@@ -191,27 +226,22 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{0};
 
-  TileRegs kbuf, vbuf;
-  int segbuf = -1;
+  auto issue = [&](int kt, uint16_t* kd, uint16_t* vd, int32_t* sd) {
+    tile_async_load(kd, Kh, kt * BK, p.Sk, wave, lane);
+    tile_async_load(vd, Vh, kt * BK, p.Sk, wave, lane);
+    if (wave == 0) vec_async_load(sd, segk_b, kt * BK, p.Sk, lane);
+  };
+
+  // One key tile: wait for its loads, start the next tile's loads into the other buffers,
+  // then S^T, mask, online softmax and O^T += V^T P^T.
   int kt = next_live(st0, st1, has_r1, lo, hi);
-  if (kt <= hi) {
-    tile_gload(kbuf, Kh, kt * BK, p.Sk, tid);
-    tile_gload(vbuf, Vh, kt * BK, p.Sk, tid);
-    if (tid < BK) segbuf = int(row_gload32(segk_b, kt * BK, p.Sk, tid));
-  }
-  while (kt <= hi) {
+  auto step = [&](const uint16_t* kb_lds, const uint16_t* vb_lds, const int32_t* sb_lds,
+                  uint16_t* kn_lds, uint16_t* vn_lds, int32_t* sn_lds) {
     const int st = uniform(combine_status(st0[kt], has_r1 ? st1[kt] : uint8_t(LWM_TILE_SKIP)));
-    __syncthreads();
-    tile_store(kbuf, k_lds, tid);
-    tile_store(vbuf, v_lds, tid);
-    if (tid < BK) segk_lds[tid] = segbuf;
-    __syncthreads();
     const int kn = next_live(st0, st1, has_r1, kt + 1, hi);
-    if (kn <= hi) {
-      tile_gload(kbuf, Kh, kn * BK, p.Sk, tid);
-      tile_gload(vbuf, Vh, kn * BK, p.Sk, tid);
-      if (tid < BK) segbuf = int(row_gload32(segk_b, kn * BK, p.Sk, tid));
-    }
+    wait_vmem();
+    __syncthreads();
+    if (kn <= hi) issue(kn, kn_lds, vn_lds, sn_lds);
 
     // S^T = K Q^T for two 32-key blocks (K rows loaded in kperm order)
     f32x16 sacc[2];
@@ -221,7 +251,7 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
       const int krow = 32 * sub + kperm(col);
 #pragma unroll
       for (int s = 0; s < D / 16; ++s)
-        sacc[sub] = mfma32(lds_load8(k_lds + tile_off(krow, 16 * s + 8 * hf)), qreg[s], sacc[sub]);
+        sacc[sub] = mfma32(lds_load8(kb_lds + tile_off(krow, 16 * s + 8 * hf)), qreg[s], sacc[sub]);
     }
 
     if (st == LWM_TILE_PARTIAL) {
@@ -232,7 +262,7 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
         for (int a = 0; a < 2; ++a) {
           const int kl0 = 32 * sub + 16 * a + 8 * hf;
           int sk8[8];
-          lds_load_i8(segk_lds + kl0, sk8);
+          lds_load_i8(sb_lds + kl0, sk8);
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int key = kt * BK + kl0 + j;
@@ -243,17 +273,18 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
         }
     }
 
-    float mx = -INFINITY;
+    // row max over the lane's 32 scores (four independent chains), then across the halves
+    float mx4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[sub][i]);
-    const float mxc = half_max(mx) * c;
+      for (int i = 0; i < 16; ++i) mx4[(i & 1) + 2 * sub] = fmaxf(mx4[(i & 1) + 2 * sub], sacc[sub][i]);
+    const float mxc = half_max(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]))) * c;
     const bool upd = mxc > m_run + kTau;  // false while every key so far is masked
     const float alpha = upd ? fast_exp2(m_run - mxc) : 1.f;
     if (upd) m_run = mxc;
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    float psum = 0.f;
+    float ps4[4] = {0.f, 0.f, 0.f, 0.f};
     bf16x8 pb[4];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
@@ -263,11 +294,11 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           pv[j] = fast_exp2(fmaf(sacc[sub][8 * a + j], c, -m_use));
-          psum += pv[j];
+          ps4[j & 3] += pv[j];
         }
         pb[2 * sub + a] = to_bf16x8(pv);
       }
-    l_run = l_run * alpha + psum;
+    l_run = l_run * alpha + ((ps4[0] + ps4[1]) + (ps4[2] + ps4[3]));
     if (__ballot(upd) != 0) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
@@ -280,8 +311,15 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
     for (int ks = 0; ks < BK / 16; ++ks)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
-        oacc[db] = mfma32(lds_load_tr8(v_lds, 16 * ks, 32 * db, lane), pb[ks], oacc[db]);
+        oacc[db] = mfma32(lds_load_tr8(vb_lds, 16 * ks, 32 * db, lane), pb[ks], oacc[db]);
     kt = kn;
+  };
+
+  if (kt <= hi) issue(kt, k_lds, v_lds, segk_lds);
+  while (kt <= hi) {
+    step(k_lds, v_lds, segk_lds, k_lds + kTileElems, v_lds + kTileElems, segk_lds + BK);
+    if (kt > hi) break;
+    step(k_lds + kTileElems, v_lds + kTileElems, segk_lds + BK, k_lds, v_lds, segk_lds);
   }
 
   const float l_tot = half_sum(l_run);
@@ -322,10 +360,12 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
 // backward
 // ---------------------------------------------------------------------------------------
 
-// Delta_i = <dO_i, O_i> (float32), 16 lanes per row of 128.
+// Delta_i = <dO_i, O_i> and LSE_i * log2(e) (both float32), 16 lanes per row of 128.
 __global__ void __launch_bounds__(NT) delta_bf16_kernel(int64_t rows, const uint16_t* __restrict__ O,
                                                         const uint16_t* __restrict__ dO,
-                                                        float* __restrict__ delta) {
+                                                        const float* __restrict__ LSE,
+                                                        float* __restrict__ delta,
+                                                        float* __restrict__ lse2) {
   const int64_t gid = int64_t(blockIdx.x) * NT + threadIdx.x;
   const int64_t row = gid >> 4;
   const int part = threadIdx.x & 15;
@@ -340,7 +380,10 @@ __global__ void __launch_bounds__(NT) delta_bf16_kernel(int64_t rows, const uint
   }
 #pragma unroll
   for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 16);
-  if (row < rows && part == 0) delta[row] = s;
+  if (row < rows && part == 0) {
+    delta[row] = s;
+    lse2[row] = LSE[row] * kLog2e;
+  }
 }
 
 // dQ: query-major like the forward.  Per key tile: S^T = K Q^T, dP^T = V dO^T,
@@ -348,12 +391,12 @@ __global__ void __launch_bounds__(NT) delta_bf16_kernel(int64_t rows, const uint
 __global__ void __launch_bounds__(NT, 2)
 dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ Q,
                const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-               const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
+               const uint16_t* __restrict__ dO, const float* __restrict__ LSE2,
                const float* __restrict__ delta, const int32_t* __restrict__ seg_q,
                const int32_t* __restrict__ seg_k, uint16_t* __restrict__ dQ) {
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[BK * D];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[BK * D];
-  __shared__ int32_t segk_lds[BK];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2 * kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2 * kTileElems];
+  __shared__ __attribute__((aligned(16))) int32_t segk_lds[2 * BK];
 
   const int idx = blockIdx.x;
   const int h = idx % p.H;
@@ -380,7 +423,7 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
     qreg[s] = *reinterpret_cast<bf16x8*>(&a);
     greg[s] = *reinterpret_cast<bf16x8*>(&g);
   }
-  const float lse2 = qlive ? LSE[r64] * kLog2e : 0.f;
+  const float lse2 = qlive ? LSE2[r64] : 0.f;
   const float dl = qlive ? delta[r64] : 0.f;
   const int32_t sq = qlive ? seg_q[int64_t(b) * p.Sq + qrow] : -1;
   const int dpos = clamp_dpos(p.q_offset, p.k_offset);
@@ -398,27 +441,20 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) dqacc[i] = f32x16{0};
 
-  TileRegs kbuf, vbuf;
-  int segbuf = -1;
+  auto issue = [&](int kt, uint16_t* kd, uint16_t* vd, int32_t* sd) {
+    tile_async_load(kd, Kh, kt * BK, p.Sk, wave, lane);
+    tile_async_load(vd, Vh, kt * BK, p.Sk, wave, lane);
+    if (wave == 0) vec_async_load(sd, segk_b, kt * BK, p.Sk, lane);
+  };
+
   int kt = next_live(st0, st1, has_r1, lo, hi);
-  if (kt <= hi) {
-    tile_gload(kbuf, Kh, kt * BK, p.Sk, tid);
-    tile_gload(vbuf, Vh, kt * BK, p.Sk, tid);
-    if (tid < BK) segbuf = int(row_gload32(segk_b, kt * BK, p.Sk, tid));
-  }
-  while (kt <= hi) {
+  auto step = [&](const uint16_t* kb_lds, const uint16_t* vb_lds, const int32_t* sb_lds,
+                  uint16_t* kn_lds, uint16_t* vn_lds, int32_t* sn_lds) {
     const int st = uniform(combine_status(st0[kt], has_r1 ? st1[kt] : uint8_t(LWM_TILE_SKIP)));
-    __syncthreads();
-    tile_store(kbuf, k_lds, tid);
-    tile_store(vbuf, v_lds, tid);
-    if (tid < BK) segk_lds[tid] = segbuf;
-    __syncthreads();
     const int kn = next_live(st0, st1, has_r1, kt + 1, hi);
-    if (kn <= hi) {
-      tile_gload(kbuf, Kh, kn * BK, p.Sk, tid);
-      tile_gload(vbuf, Vh, kn * BK, p.Sk, tid);
-      if (tid < BK) segbuf = int(row_gload32(segk_b, kn * BK, p.Sk, tid));
-    }
+    wait_vmem();
+    __syncthreads();
+    if (kn <= hi) issue(kn, kn_lds, vn_lds, sn_lds);
 
     bf16x8 dsb[4];
 #pragma unroll
@@ -428,15 +464,15 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
         const int off = tile_off(krow, 16 * s + 8 * hf);
-        sacc = mfma32(lds_load8(k_lds + off), qreg[s], sacc);
-        pacc = mfma32(lds_load8(v_lds + off), greg[s], pacc);
+        sacc = mfma32(lds_load8(kb_lds + off), qreg[s], sacc);
+        pacc = mfma32(lds_load8(vb_lds + off), greg[s], pacc);
       }
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         float ds[8];
         const int kl0 = 32 * sub + 16 * a + 8 * hf;
         int sk8[8];
-        if (st == LWM_TILE_PARTIAL) lds_load_i8(segk_lds + kl0, sk8);
+        if (st == LWM_TILE_PARTIAL) lds_load_i8(sb_lds + kl0, sk8);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int i = 8 * a + j;
@@ -456,8 +492,18 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
     for (int ks = 0; ks < BK / 16; ++ks)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
-        dqacc[db] = mfma32(lds_load_tr8(k_lds, 16 * ks, 32 * db, lane), dsb[ks], dqacc[db]);
+        dqacc[db] = mfma32(lds_load_tr8(kb_lds, 16 * ks, 32 * db, lane), dsb[ks], dqacc[db]);
     kt = kn;
+  };
+
+  // one loop body with a run-time buffer half (keeps a single set of LDS addresses live)
+  if (kt <= hi) issue(kt, k_lds, v_lds, segk_lds);
+  int half = 0;
+  while (kt <= hi) {
+    const int cur = half * kTileElems, nxt = (half ^ 1) * kTileElems;
+    step(k_lds + cur, v_lds + cur, segk_lds + half * BK, k_lds + nxt, v_lds + nxt,
+         segk_lds + (half ^ 1) * BK);
+    half ^= 1;
   }
   if (!qlive) return;
   uint16_t* out = dQ + r64 * D;
@@ -479,15 +525,14 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
 __global__ void __launch_bounds__(NT, 1)
 dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__ Q,
                 const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-                const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
+                const uint16_t* __restrict__ dO, const float* __restrict__ LSE2,
                 const float* __restrict__ delta, const int32_t* __restrict__ seg_q,
                 const int32_t* __restrict__ seg_k, uint16_t* __restrict__ dK,
                 uint16_t* __restrict__ dV) {
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[TB * D];
-  __shared__ __attribute__((aligned(16))) uint16_t g_lds[TB * D];
-  __shared__ __attribute__((aligned(16))) float lse_lds[TB];
-  __shared__ __attribute__((aligned(16))) float dl_lds[TB];
-  __shared__ int32_t segq_lds[TB];
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[2 * kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t g_lds[2 * kTileElems];
+  // per query row of the tile: LSE*log2(e), Delta and the segment id (as raw 32-bit words)
+  __shared__ __attribute__((aligned(16))) float row_lds[2 * 3 * TB];
 
   const int idx = blockIdx.x;
   const int h = idx % p.H;
@@ -498,7 +543,7 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
   const int64_t bh = int64_t(b) * p.H + h;
   const uint16_t* Qh = Q + bh * p.Sq * D;
   const uint16_t* Gh = dO + bh * p.Sq * D;
-  const float* lse_h = LSE + bh * p.Sq;
+  const float* lse_h = LSE2 + bh * p.Sq;
   const float* dl_h = delta + bh * p.Sq;
   const int32_t* segq_b = seg_q + int64_t(b) * p.Sq;
 
@@ -534,34 +579,23 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
     dvacc[i] = f32x16{0};
   }
 
-  TileRegs qbuf, gbuf;
-  float lsebuf = 0.f, dlbuf = 0.f;
-  int segbuf = -1;
-  auto gload_all = [&](int qb) {
-    tile_gload(qbuf, Qh, qb * TB, p.Sq, tid);
-    tile_gload(gbuf, Gh, qb * TB, p.Sq, tid);
-    if (tid < TB) {
-      lsebuf = __uint_as_float(row_gload32(lse_h, qb * TB, p.Sq, tid)) * kLog2e;
-      dlbuf = __uint_as_float(row_gload32(dl_h, qb * TB, p.Sq, tid));
-      segbuf = int(row_gload32(segq_b, qb * TB, p.Sq, tid));
-    }
+  auto issue = [&](int qb, uint16_t* qd, uint16_t* gd, float* rd) {
+    tile_async_load(qd, Qh, qb * TB, p.Sq, wave, lane);
+    tile_async_load(gd, Gh, qb * TB, p.Sq, wave, lane);
+    if (wave == 0) vec_async_load(rd, lse_h, qb * TB, p.Sq, lane);
+    if (wave == 1) vec_async_load(rd + TB, dl_h, qb * TB, p.Sq, lane);
+    if (wave == 2) vec_async_load(rd + 2 * TB, segq_b, qb * TB, p.Sq, lane);
   };
+
   int qb = next_live_col(stb, t.nkb, c0, has_c1, lo, hi);
-  if (qb <= hi) gload_all(qb);
-  while (qb <= hi) {
+  auto step = [&](const uint16_t* qb_lds, const uint16_t* gb_lds, const float* rb_lds,
+                  uint16_t* qn_lds, uint16_t* gn_lds, float* rn_lds) {
     const uint8_t* row = stb + int64_t(qb) * t.nkb;
     const int st = uniform(combine_status(row[c0], has_c1 ? row[c0 + 1] : uint8_t(LWM_TILE_SKIP)));
-    __syncthreads();
-    tile_store(qbuf, q_lds, tid);
-    tile_store(gbuf, g_lds, tid);
-    if (tid < TB) {
-      lse_lds[tid] = lsebuf;
-      dl_lds[tid] = dlbuf;
-      segq_lds[tid] = segbuf;
-    }
-    __syncthreads();
     const int qn = next_live_col(stb, t.nkb, c0, has_c1, qb + 1, hi);
-    if (qn <= hi) gload_all(qn);
+    wait_vmem();
+    __syncthreads();
+    if (qn <= hi) issue(qn, qn_lds, gn_lds, rn_lds);
 
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -570,22 +604,20 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
         const int off = tile_off(qrow, 16 * s + 8 * hf);
-        sacc = mfma32(lds_load8(q_lds + off), kreg[s], sacc);
-        pacc = mfma32(lds_load8(g_lds + off), vreg[s], pacc);
+        sacc = mfma32(lds_load8(qb_lds + off), kreg[s], sacc);
+        pacc = mfma32(lds_load8(gb_lds + off), vreg[s], pacc);
       }
       bf16x8 pb[2], dsb[2];
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         const int qbase = 32 * sub + 16 * a + 8 * hf;  // 8 consecutive local query rows
-        const float4 l0 = *reinterpret_cast<const float4*>(lse_lds + qbase);
-        const float4 l1 = *reinterpret_cast<const float4*>(lse_lds + qbase + 4);
-        const float4 d0 = *reinterpret_cast<const float4*>(dl_lds + qbase);
-        const float4 d1 = *reinterpret_cast<const float4*>(dl_lds + qbase + 4);
-        const float lsev[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-        const float dlv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+        float lsev[8], dlv[8];
+        lds_load_f8(rb_lds + qbase, lsev);
+        lds_load_f8(rb_lds + TB + qbase, dlv);
         float pv[8], ds[8];
         int sq8[8];
-        if (st == LWM_TILE_PARTIAL) lds_load_i8(segq_lds + qbase, sq8);
+        if (st == LWM_TILE_PARTIAL)
+          lds_load_i8(reinterpret_cast<const int32_t*>(rb_lds + 2 * TB) + qbase, sq8);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int i = 8 * a + j;
@@ -608,12 +640,22 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
         const int ks = 2 * sub + a;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          dvacc[db] = mfma32(lds_load_tr8(g_lds, 16 * ks, 32 * db, lane), pb[a], dvacc[db]);
-          dkacc[db] = mfma32(lds_load_tr8(q_lds, 16 * ks, 32 * db, lane), dsb[a], dkacc[db]);
+          dvacc[db] = mfma32(lds_load_tr8(gb_lds, 16 * ks, 32 * db, lane), pb[a], dvacc[db]);
+          dkacc[db] = mfma32(lds_load_tr8(qb_lds, 16 * ks, 32 * db, lane), dsb[a], dkacc[db]);
         }
       }
     }
     qb = qn;
+  };
+
+  // one loop body with a run-time buffer half (keeps a single set of LDS addresses live)
+  if (qb <= hi) issue(qb, q_lds, g_lds, row_lds);
+  int half = 0;
+  while (qb <= hi) {
+    const int cur = half * kTileElems, nxt = (half ^ 1) * kTileElems;
+    step(q_lds + cur, g_lds + cur, row_lds + half * 3 * TB, q_lds + nxt, g_lds + nxt,
+         row_lds + (half ^ 1) * 3 * TB);
+    half ^= 1;
   }
   if (!klive) return;
   uint16_t* ko = dK + k64 * D;
@@ -650,27 +692,30 @@ hipError_t launch_fwd_bf16(const lwm_attn_desc& d, int mode, const void* q, cons
   return hipGetLastError();
 }
 
+// Workspace: Delta [rows] then LSE * log2(e) [rows], rows = B*H*Sq, each 256-byte aligned.
 hipError_t launch_bwd_bf16(const lwm_attn_desc& d, int phase, const void* q, const void* k,
                            const void* v, const void* o, const void* dO, const float* lse,
                            const int32_t* seg_q, const int32_t* seg_k, const void* table,
-                           void* dq, void* dk, void* dv, float* delta, hipStream_t stream) {
+                           void* dq, void* dk, void* dv, float* workspace, hipStream_t stream) {
   const TableView t = table_view(d, table);
   const AttnParams p = attn_params(d);
   const int64_t rows = int64_t(d.B) * d.H * d.Sq;
+  float* delta = workspace;
+  float* lse2 = workspace + align256(size_t(rows) * sizeof(float)) / sizeof(float);
   if (phase < 0 || phase == LWM_BWD_DELTA)
     delta_bf16_kernel<<<dim3(unsigned((rows * 16 + NT - 1) / NT)), dim3(NT), 0, stream>>>(
-        rows, static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dO), delta);
+        rows, static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dO), lse, delta, lse2);
   const int nqt = (d.Sq + BQ - 1) / BQ;
   if (phase < 0 || phase == LWM_BWD_DQ)
     dq_bf16_kernel<<<dim3(unsigned(int64_t(nqt) * d.H * d.B)), dim3(NT), 0, stream>>>(
         p, t, nqt, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-        static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), lse, delta, seg_q,
+        static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), lse2, delta, seg_q,
         seg_k, static_cast<uint16_t*>(dq));
   const int nkt = (d.Sk + 127) / 128;
   if (phase < 0 || phase == LWM_BWD_DKV)
     dkv_bf16_kernel<<<dim3(unsigned(int64_t(nkt) * d.H * d.B)), dim3(NT), 0, stream>>>(
         p, t, nkt, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-        static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), lse, delta, seg_q,
+        static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), lse2, delta, seg_q,
         seg_k, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv));
   return hipGetLastError();
 }

@@ -86,7 +86,7 @@ hipError_t launch_fwd_bf16(const lwm_attn_desc& d, int mode, const void* q, cons
 hipError_t launch_bwd_bf16(const lwm_attn_desc& d, int phase, const void* q, const void* k, const void* v,
                            const void* o, const void* dO, const float* lse,
                            const int32_t* seg_q, const int32_t* seg_k, const void* table,
-                           void* dq, void* dk, void* dv, float* delta, hipStream_t stream);
+                           void* dq, void* dk, void* dv, float* workspace, hipStream_t stream);
 
 hipError_t launch_merge(int64_t rows, int32_t D, float* m, float* l, float* acc, const float* mc,
                         const float* lc, const float* accc, int32_t finalize, int32_t out_dtype,

@@ -75,7 +75,7 @@ def test_table_bytes_follow_documented_layout(lib):
         expect = al(B * nqb * 8) + al(B * nkb * 8) + al(B * nqb * nkb) + al(B * nqb * 16) + al(B * nkb * 16)
         assert lwm.lwm_attn_block_table_bytes(d) == expect
     assert lwm.lwm_attn_block_table_bytes(desc(block_q=48)) == 0
-    assert lwm.lwm_attn_bwd_workspace_bytes(desc(B=2, H=3, Sq=100)) == al(2 * 3 * 100 * 4)
+    assert lwm.lwm_attn_bwd_workspace_bytes(desc(B=2, H=3, Sq=100)) == 2 * al(2 * 3 * 100 * 4)
 
 
 def call_fwd(lib, d, mode=0, q=FAKE, k=FAKE, v=FAKE, sq=FAKE, sk=FAKE, t=FAKE, o=FAKE, lse=FAKE,
