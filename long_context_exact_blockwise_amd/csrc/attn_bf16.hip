@@ -394,9 +394,14 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
                const uint16_t* __restrict__ dO, const float* __restrict__ LSE2,
                const float* __restrict__ delta, const int32_t* __restrict__ seg_q,
                const int32_t* __restrict__ seg_k, uint16_t* __restrict__ dQ) {
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2 * kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2 * kTileElems];
+  // [K tile | V tile] per buffer half in one array, so V reads reuse the K read addresses
+  // with a constant offset
+  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[4 * kTileElems];
   __shared__ __attribute__((aligned(16))) int32_t segk_lds[2 * BK];
+  uint16_t* const k_lds0 = kv_lds;
+  uint16_t* const v_lds0 = kv_lds + kTileElems;
+  uint16_t* const k_lds1 = kv_lds + 2 * kTileElems;
+  uint16_t* const v_lds1 = kv_lds + 3 * kTileElems;
 
   const int idx = blockIdx.x;
   const int h = idx % p.H;
@@ -487,6 +492,9 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
         }
         dsb[2 * sub + a] = to_bf16x8(ds);
       }
+      // keep the two 32-key halves apart: overlapping them would need a second set of
+      // score registers, which does not fit beside two waves per SIMD
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks)
@@ -496,14 +504,11 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
     kt = kn;
   };
 
-  // one loop body with a run-time buffer half (keeps a single set of LDS addresses live)
-  if (kt <= hi) issue(kt, k_lds, v_lds, segk_lds);
-  int half = 0;
+  if (kt <= hi) issue(kt, k_lds0, v_lds0, segk_lds);
   while (kt <= hi) {
-    const int cur = half * kTileElems, nxt = (half ^ 1) * kTileElems;
-    step(k_lds + cur, v_lds + cur, segk_lds + half * BK, k_lds + nxt, v_lds + nxt,
-         segk_lds + (half ^ 1) * BK);
-    half ^= 1;
+    step(k_lds0, v_lds0, segk_lds, k_lds1, v_lds1, segk_lds + BK);
+    if (kt > hi) break;
+    step(k_lds1, v_lds1, segk_lds + BK, k_lds0, v_lds0, segk_lds);
   }
   if (!qlive) return;
   uint16_t* out = dQ + r64 * D;
@@ -529,8 +534,12 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
                 const float* __restrict__ delta, const int32_t* __restrict__ seg_q,
                 const int32_t* __restrict__ seg_k, uint16_t* __restrict__ dK,
                 uint16_t* __restrict__ dV) {
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[2 * kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t g_lds[2 * kTileElems];
+  // [Q tile | dO tile] per buffer half in one array, so dO reads reuse the Q read addresses
+  // with a constant offset
+  __shared__ __attribute__((aligned(16))) uint16_t qg_lds[4 * kTileElems];
+  uint16_t* const q_lds0 = qg_lds;
+  uint16_t* const g_lds0 = qg_lds + kTileElems;
+
   // per query row of the tile: LSE*log2(e), Delta and the segment id (as raw 32-bit words)
   __shared__ __attribute__((aligned(16))) float row_lds[2 * 3 * TB];
 
@@ -649,12 +658,12 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
   };
 
   // one loop body with a run-time buffer half (keeps a single set of LDS addresses live)
-  if (qb <= hi) issue(qb, q_lds, g_lds, row_lds);
+  if (qb <= hi) issue(qb, q_lds0, g_lds0, row_lds);
   int half = 0;
   while (qb <= hi) {
-    const int cur = half * kTileElems, nxt = (half ^ 1) * kTileElems;
-    step(q_lds + cur, g_lds + cur, row_lds + half * 3 * TB, q_lds + nxt, g_lds + nxt,
-         row_lds + (half ^ 1) * 3 * TB);
+    const int cur = half * 2 * kTileElems, nxt = (half ^ 1) * 2 * kTileElems;
+    step(qg_lds + cur, qg_lds + cur + kTileElems, row_lds + half * 3 * TB, qg_lds + nxt,
+         qg_lds + nxt + kTileElems, row_lds + (half ^ 1) * 3 * TB);
     half ^= 1;
   }
   if (!klive) return;
