@@ -69,23 +69,29 @@ __device__ __forceinline__ void range_union(const int32_t* a, const int32_t* b, 
   }
 }
 
-// First non-SKIP tile at or after kt in [kt, hi] (hi + 1 if none) of a pair of table rows.
-__device__ __forceinline__ int next_live(const uint8_t* s0, const uint8_t* s1, bool has1, int kt,
-                                         int hi) {
-  while (kt <= hi && combine_status(s0[kt], has1 ? s1[kt] : uint8_t(LWM_TILE_SKIP)) == LWM_TILE_SKIP)
-    ++kt;
-  return uniform(kt);
+// The combined status of the tiles a workgroup visits is staged in LDS, one byte per tile,
+// in chunks of kStatChunk tiles: scanning for the next live tile then costs LDS reads
+// instead of a dependent global-memory round trip per tile.
+constexpr int kStatChunk = 2048;
+
+__device__ __forceinline__ void stage_status_rows(uint8_t* stat, const uint8_t* s0, const uint8_t* s1,
+                                                  bool has1, int c0, int c1, int tid) {
+  for (int i = tid; i <= c1 - c0; i += NT)
+    stat[i] = combine_status(s0[c0 + i], has1 ? s1[c0 + i] : uint8_t(LWM_TILE_SKIP));
 }
 
-// Same over a pair of table columns (stride nkb between rows).
-__device__ __forceinline__ int next_live_col(const uint8_t* base, int64_t nkb, int c0, bool has1,
-                                             int qb, int hi) {
-  while (qb <= hi) {
-    const uint8_t* row = base + qb * nkb;
-    if (combine_status(row[c0], has1 ? row[c0 + 1] : uint8_t(LWM_TILE_SKIP)) != LWM_TILE_SKIP) break;
-    ++qb;
+__device__ __forceinline__ void stage_status_cols(uint8_t* stat, const uint8_t* base, int64_t nkb,
+                                                  int col0, bool has1, int c0, int c1, int tid) {
+  for (int i = tid; i <= c1 - c0; i += NT) {
+    const uint8_t* row = base + int64_t(c0 + i) * nkb;
+    stat[i] = combine_status(row[col0], has1 ? row[col0 + 1] : uint8_t(LWM_TILE_SKIP));
   }
-  return uniform(qb);
+}
+
+// First tile k' >= k in [k, c1] whose staged status is not SKIP (c1 + 1 if none).
+__device__ __forceinline__ int next_live_lds(const uint8_t* stat, int c0, int k, int c1) {
+  while (k <= c1 && stat[k - c0] == LWM_TILE_SKIP) ++k;
+  return uniform(k);
 }
 
 // Position difference q_offset - k_offset clamped into int32: with it, key j is causally
@@ -184,6 +190,7 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2 * kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2 * kTileElems];
   __shared__ __attribute__((aligned(16))) int32_t segk_lds[2 * BK];
+  __shared__ uint8_t stat_lds[kStatChunk];
 
   // Longest rows first: rank 0 is the last query tile; heads are interleaved so that
   // consecutive workgroups (spread over the XCDs) share a tile rank.
@@ -234,16 +241,17 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
 
   // One key tile: wait for its loads, start the next tile's loads into the other buffers,
   // then S^T, mask, online softmax and O^T += V^T P^T.
-  int kt = next_live(st0, st1, has_r1, lo, hi);
+  int kt = 0, c0 = 0, c1 = -1;
   auto step = [&](const uint16_t* kb_lds, const uint16_t* vb_lds, const int32_t* sb_lds,
                   uint16_t* kn_lds, uint16_t* vn_lds, int32_t* sn_lds) {
-    const int st = uniform(combine_status(st0[kt], has_r1 ? st1[kt] : uint8_t(LWM_TILE_SKIP)));
-    const int kn = next_live(st0, st1, has_r1, kt + 1, hi);
+    const int st = uniform(stat_lds[kt - c0]);
+    const int kn = next_live_lds(stat_lds, c0, kt + 1, c1);
     wait_vmem();
     __syncthreads();
-    if (kn <= hi) issue(kn, kn_lds, vn_lds, sn_lds);
+    if (kn <= c1) issue(kn, kn_lds, vn_lds, sn_lds);
 
-    // S^T = K Q^T for two 32-key blocks (K rows loaded in kperm order)
+    // S^T = K Q^T for two 32-key blocks (K rows loaded in kperm order).  The operand reads
+    // run four MFMAs ahead so LDS latency hides behind the matrix pipe.
     f32x16 sacc[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -253,6 +261,13 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
       for (int s = 0; s < D / 16; ++s)
         sacc[sub] = mfma32(lds_load8(kb_lds + tile_off(krow, 16 * s + 8 * hf)), qreg[s], sacc[sub]);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
 
     if (st == LWM_TILE_PARTIAL) {
       // branch-free visibility; rows past Sq carry sq = -1 and see nothing
@@ -306,20 +321,35 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
     }
 
-    // O^T += V^T P^T over four 16-key steps; V^T read transposed from the row-major tile
+    // O^T += V^T P^T over four 16-key steps; V^T read transposed from the row-major tile,
+    // operand reads four MFMAs ahead
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
         oacc[db] = mfma32(lds_load_tr8(vb_lds, 16 * ks, 32 * db, lane), pb[ks], oacc[db]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 2);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 2);
     kt = kn;
   };
 
-  if (kt <= hi) issue(kt, k_lds, v_lds, segk_lds);
-  while (kt <= hi) {
-    step(k_lds, v_lds, segk_lds, k_lds + kTileElems, v_lds + kTileElems, segk_lds + BK);
-    if (kt > hi) break;
-    step(k_lds + kTileElems, v_lds + kTileElems, segk_lds + BK, k_lds, v_lds, segk_lds);
+  for (c0 = lo; c0 <= hi; c0 += kStatChunk) {
+    c1 = min(hi, c0 + kStatChunk - 1);
+    __syncthreads();
+    stage_status_rows(stat_lds, st0, st1, has_r1, c0, c1, tid);
+    __syncthreads();
+    kt = next_live_lds(stat_lds, c0, c0, c1);
+    if (kt <= c1) issue(kt, k_lds, v_lds, segk_lds);
+    while (kt <= c1) {
+      step(k_lds, v_lds, segk_lds, k_lds + kTileElems, v_lds + kTileElems, segk_lds + BK);
+      if (kt > c1) break;
+      step(k_lds + kTileElems, v_lds + kTileElems, segk_lds + BK, k_lds, v_lds, segk_lds);
+    }
   }
 
   const float l_tot = half_sum(l_run);
@@ -398,6 +428,7 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
   // with a constant offset
   __shared__ __attribute__((aligned(16))) uint16_t kv_lds[4 * kTileElems];
   __shared__ __attribute__((aligned(16))) int32_t segk_lds[2 * BK];
+  __shared__ uint8_t stat_lds[kStatChunk];
   uint16_t* const k_lds0 = kv_lds;
   uint16_t* const v_lds0 = kv_lds + kTileElems;
   uint16_t* const k_lds1 = kv_lds + 2 * kTileElems;
@@ -452,26 +483,28 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
     if (wave == 0) vec_async_load(sd, segk_b, kt * BK, p.Sk, lane);
   };
 
-  int kt = next_live(st0, st1, has_r1, lo, hi);
+  int kt = 0, c0 = 0, c1 = -1;
   auto step = [&](const uint16_t* kb_lds, const uint16_t* vb_lds, const int32_t* sb_lds,
                   uint16_t* kn_lds, uint16_t* vn_lds, int32_t* sn_lds) {
-    const int st = uniform(combine_status(st0[kt], has_r1 ? st1[kt] : uint8_t(LWM_TILE_SKIP)));
-    const int kn = next_live(st0, st1, has_r1, kt + 1, hi);
+    const int st = uniform(stat_lds[kt - c0]);
+    const int kn = next_live_lds(stat_lds, c0, kt + 1, c1);
     wait_vmem();
     __syncthreads();
-    if (kn <= hi) issue(kn, kn_lds, vn_lds, sn_lds);
+    if (kn <= c1) issue(kn, kn_lds, vn_lds, sn_lds);
 
     bf16x8 dsb[4];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       f32x16 sacc = f32x16{0}, pacc = f32x16{0};
       const int krow = 32 * sub + kperm(col);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
         const int off = tile_off(krow, 16 * s + 8 * hf);
         sacc = mfma32(lds_load8(kb_lds + off), qreg[s], sacc);
         pacc = mfma32(lds_load8(vb_lds + off), greg[s], pacc);
       }
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         float ds[8];
@@ -496,19 +529,28 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
       // score registers, which does not fit beside two waves per SIMD
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
         dqacc[db] = mfma32(lds_load_tr8(kb_lds, 16 * ks, 32 * db, lane), dsb[ks], dqacc[db]);
+    __builtin_amdgcn_s_setprio(0);
     kt = kn;
   };
 
-  if (kt <= hi) issue(kt, k_lds0, v_lds0, segk_lds);
-  while (kt <= hi) {
-    step(k_lds0, v_lds0, segk_lds, k_lds1, v_lds1, segk_lds + BK);
-    if (kt > hi) break;
-    step(k_lds1, v_lds1, segk_lds + BK, k_lds0, v_lds0, segk_lds);
+  for (c0 = lo; c0 <= hi; c0 += kStatChunk) {
+    c1 = min(hi, c0 + kStatChunk - 1);
+    __syncthreads();
+    stage_status_rows(stat_lds, st0, st1, has_r1, c0, c1, tid);
+    __syncthreads();
+    kt = next_live_lds(stat_lds, c0, c0, c1);
+    if (kt <= c1) issue(kt, k_lds0, v_lds0, segk_lds);
+    while (kt <= c1) {
+      step(k_lds0, v_lds0, segk_lds, k_lds1, v_lds1, segk_lds + BK);
+      if (kt > c1) break;
+      step(k_lds1, v_lds1, segk_lds + BK, k_lds0, v_lds0, segk_lds);
+    }
   }
   if (!qlive) return;
   uint16_t* out = dQ + r64 * D;
@@ -542,6 +584,7 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
 
   // per query row of the tile: LSE*log2(e), Delta and the segment id (as raw 32-bit words)
   __shared__ __attribute__((aligned(16))) float row_lds[2 * 3 * TB];
+  __shared__ uint8_t stat_lds[kStatChunk];
 
   const int idx = blockIdx.x;
   const int h = idx % p.H;
@@ -596,15 +639,14 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
     if (wave == 2) vec_async_load(rd + 2 * TB, segq_b, qb * TB, p.Sq, lane);
   };
 
-  int qb = next_live_col(stb, t.nkb, c0, has_c1, lo, hi);
+  int qb = 0, w0 = 0, w1 = -1;
   auto step = [&](const uint16_t* qb_lds, const uint16_t* gb_lds, const float* rb_lds,
                   uint16_t* qn_lds, uint16_t* gn_lds, float* rn_lds) {
-    const uint8_t* row = stb + int64_t(qb) * t.nkb;
-    const int st = uniform(combine_status(row[c0], has_c1 ? row[c0 + 1] : uint8_t(LWM_TILE_SKIP)));
-    const int qn = next_live_col(stb, t.nkb, c0, has_c1, qb + 1, hi);
+    const int st = uniform(stat_lds[qb - w0]);
+    const int qn = next_live_lds(stat_lds, w0, qb + 1, w1);
     wait_vmem();
     __syncthreads();
-    if (qn <= hi) issue(qn, qn_lds, gn_lds, rn_lds);
+    if (qn <= w1) issue(qn, qn_lds, gn_lds, rn_lds);
 
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -657,14 +699,21 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
     qb = qn;
   };
 
-  // one loop body with a run-time buffer half (keeps a single set of LDS addresses live)
-  if (qb <= hi) issue(qb, q_lds0, g_lds0, row_lds);
-  int half = 0;
-  while (qb <= hi) {
-    const int cur = half * 2 * kTileElems, nxt = (half ^ 1) * 2 * kTileElems;
-    step(qg_lds + cur, qg_lds + cur + kTileElems, row_lds + half * 3 * TB, qg_lds + nxt,
-         qg_lds + nxt + kTileElems, row_lds + (half ^ 1) * 3 * TB);
-    half ^= 1;
+  for (w0 = lo; w0 <= hi; w0 += kStatChunk) {
+    w1 = min(hi, w0 + kStatChunk - 1);
+    __syncthreads();
+    stage_status_cols(stat_lds, stb, t.nkb, c0, has_c1, w0, w1, tid);
+    __syncthreads();
+    qb = next_live_lds(stat_lds, w0, w0, w1);
+    // one loop body with a run-time buffer half (keeps a single set of LDS addresses live)
+    if (qb <= w1) issue(qb, q_lds0, g_lds0, row_lds);
+    int half = 0;
+    while (qb <= w1) {
+      const int cur = half * 2 * kTileElems, nxt = (half ^ 1) * 2 * kTileElems;
+      step(qg_lds + cur, qg_lds + cur + kTileElems, row_lds + half * 3 * TB, qg_lds + nxt,
+           qg_lds + nxt + kTileElems, row_lds + (half ^ 1) * 3 * TB);
+      half ^= 1;
+    }
   }
   if (!klive) return;
   uint16_t* ko = dK + k64 * D;
