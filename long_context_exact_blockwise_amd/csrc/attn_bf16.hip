@@ -101,6 +101,27 @@ __device__ __forceinline__ int clamp_dpos(int64_t q_offset, int64_t k_offset) {
   return int(d > INT32_MAX ? INT32_MAX : (d < INT32_MIN + 1 ? INT32_MIN + 1 : d));
 }
 
+// Visibility inside a PARTIAL tile, segments aside, reduced to one compare per score.
+// key_limit: key key0 + o (o in 0..63) is visible from query row qrow iff o <= the result
+// (key bound Sk and, when causal, key - qrow <= dpos); -1 when the row sees nothing.
+__device__ __forceinline__ int key_limit(int key0, int qrow, int dpos, int Sk, int causal, bool live) {
+  int64_t lim = int64_t(Sk) - 1 - key0;
+  if (causal) lim = min(lim, int64_t(qrow) + dpos - key0);
+  if (!live) lim = -1;
+  return int(max<int64_t>(-1, min<int64_t>(64, lim)));
+}
+
+// row_window: query row row0 + o (o in 0..63) sees key `key` iff lo <= o <= hi (row bound Sq
+// and, when causal, key - row <= dpos); an empty window when the key is dead.
+__device__ __forceinline__ void row_window(int row0, int key, int dpos, int Sq, int causal, bool live,
+                                           int& lo, int& hi) {
+  const int64_t h = int64_t(Sq) - 1 - row0;
+  int64_t l = causal ? int64_t(key) - dpos - row0 : -1;
+  if (!live) l = 64;
+  lo = int(max<int64_t>(-1, min<int64_t>(64, l)));
+  hi = int(max<int64_t>(-1, min<int64_t>(64, h)));
+}
+
 // Eight consecutive int32 / float from LDS (16-byte aligned).
 __device__ __forceinline__ void lds_load_i8(const int32_t* p, int* v) {
   const int4 a = *reinterpret_cast<const int4*>(p);
@@ -271,18 +292,16 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
 
     if (st == LWM_TILE_PARTIAL) {
       // branch-free visibility; rows past Sq carry sq = -1 and see nothing
+      const int lim = key_limit(kt * BK + 8 * hf, qrow, dpos, p.Sk, p.causal, sq >= 0);
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
-          const int kl0 = 32 * sub + 16 * a + 8 * hf;
           int sk8[8];
-          lds_load_i8(sb_lds + kl0, sk8);
+          lds_load_i8(sb_lds + 32 * sub + 16 * a + 8 * hf, sk8);
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            const int key = kt * BK + kl0 + j;
-            const bool vis = (key < p.Sk) & (sk8[j] == sq) & (sq >= 0) &
-                             ((p.causal == 0) | (key - qrow <= dpos));
+            const bool vis = (sk8[j] == sq) & (32 * sub + 16 * a + j <= lim);
             sacc[sub][8 * a + j] = vis ? sacc[sub][8 * a + j] : -INFINITY;
           }
         }
@@ -412,7 +431,10 @@ __global__ void __launch_bounds__(NT) delta_bf16_kernel(int64_t rows, const uint
   for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 16);
   if (row < rows && part == 0) {
     delta[row] = s;
-    lse2[row] = LSE[row] * kLog2e;
+    // a row that sees no key (LSE = -inf) gets +inf, so exp2(s c - lse2) is 0 for every
+    // key of it, masked or not, and never inf - inf
+    const float l = LSE[row];
+    lse2[row] = l == -INFINITY ? INFINITY : l * kLog2e;
   }
 }
 
@@ -505,23 +527,27 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
         pacc = mfma32(lds_load8(vb_lds + off), greg[s], pacc);
       }
       __builtin_amdgcn_s_setprio(0);
+      if (st == LWM_TILE_PARTIAL) {
+        // hidden scores become -inf, so their probabilities come out as exactly 0
+        const int lim = key_limit(kt * BK + 8 * hf, qrow, dpos, p.Sk, p.causal, sq >= 0);
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          int sk8[8];
+          lds_load_i8(sb_lds + 32 * sub + 16 * a + 8 * hf, sk8);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const bool vis = (sk8[j] == sq) & (32 * sub + 16 * a + j <= lim);
+            sacc[8 * a + j] = vis ? sacc[8 * a + j] : -INFINITY;
+          }
+        }
+      }
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         float ds[8];
-        const int kl0 = 32 * sub + 16 * a + 8 * hf;
-        int sk8[8];
-        if (st == LWM_TILE_PARTIAL) lds_load_i8(sb_lds + kl0, sk8);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int i = 8 * a + j;
-          float pr = fast_exp2(fmaf(sacc[i], c, -lse2));
-          if (st == LWM_TILE_PARTIAL) {
-            const int key = kt * BK + kl0 + j;
-            const bool vis = (key < p.Sk) & (sk8[j] == sq) & (sq >= 0) &
-                             ((p.causal == 0) | (key - qrow <= dpos));
-            pr = vis ? pr : 0.f;
-          }
-          ds[j] = pr * (pacc[i] - dl);
+          ds[j] = fast_exp2(fmaf(sacc[i], c, -lse2)) * (pacc[i] - dl);
         }
         dsb[2 * sub + a] = to_bf16x8(ds);
       }
@@ -658,6 +684,23 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
         sacc = mfma32(lds_load8(qb_lds + off), kreg[s], sacc);
         pacc = mfma32(lds_load8(gb_lds + off), vreg[s], pacc);
       }
+      if (st == LWM_TILE_PARTIAL) {
+        // hidden scores become -inf, so their probabilities come out as exactly 0; keys
+        // past Sk carry sk = -2 and see no row
+        int rlo, rhi;
+        row_window(qb * TB + 8 * hf, key, dpos, p.Sq, p.causal, sk >= 0, rlo, rhi);
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          int sq8[8];
+          lds_load_i8(reinterpret_cast<const int32_t*>(rb_lds + 2 * TB) + 32 * sub + 16 * a + 8 * hf, sq8);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int o = 32 * sub + 16 * a + j;
+            const bool vis = (sq8[j] == sk) & (o >= rlo) & (o <= rhi);
+            sacc[8 * a + j] = vis ? sacc[8 * a + j] : -INFINITY;
+          }
+        }
+      }
       bf16x8 pb[2], dsb[2];
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
@@ -666,22 +709,11 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
         lds_load_f8(rb_lds + qbase, lsev);
         lds_load_f8(rb_lds + TB + qbase, dlv);
         float pv[8], ds[8];
-        int sq8[8];
-        if (st == LWM_TILE_PARTIAL)
-          lds_load_i8(reinterpret_cast<const int32_t*>(rb_lds + 2 * TB) + qbase, sq8);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int i = 8 * a + j;
-          float pr = fast_exp2(fmaf(sacc[i], c, -lsev[j]));
-          if (st == LWM_TILE_PARTIAL) {
-            // keys past Sk carry sk = -2 and rows past Sq fail qr < Sq
-            const int qr = qb * TB + qbase + j;
-            const bool vis = (qr < p.Sq) & (sq8[j] == sk) & (sk >= 0) &
-                             ((p.causal == 0) | (key - qr <= dpos));
-            pr = vis ? pr : 0.f;
-          }
-          pv[j] = pr;
-          ds[j] = pr * (pacc[i] - dlv[j]);
+          pv[j] = fast_exp2(fmaf(sacc[i], c, -lsev[j]));
+          ds[j] = pv[j] * (pacc[i] - dlv[j]);
         }
         pb[a] = to_bf16x8(pv);
         dsb[a] = to_bf16x8(ds);
