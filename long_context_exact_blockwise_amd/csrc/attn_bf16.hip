@@ -737,14 +737,12 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
     stage_status_cols(stat_lds, stb, t.nkb, c0, has_c1, w0, w1, tid);
     __syncthreads();
     qb = next_live_lds(stat_lds, w0, w0, w1);
-    // one loop body with a run-time buffer half (keeps a single set of LDS addresses live)
+    // unrolled by two, so every LDS address is a register plus a constant offset
     if (qb <= w1) issue(qb, q_lds0, g_lds0, row_lds);
-    int half = 0;
     while (qb <= w1) {
-      const int cur = half * 2 * kTileElems, nxt = (half ^ 1) * 2 * kTileElems;
-      step(qg_lds + cur, qg_lds + cur + kTileElems, row_lds + half * 3 * TB, qg_lds + nxt,
-           qg_lds + nxt + kTileElems, row_lds + (half ^ 1) * 3 * TB);
-      half ^= 1;
+      step(q_lds0, g_lds0, row_lds, q_lds0 + 2 * kTileElems, g_lds0 + 2 * kTileElems, row_lds + 3 * TB);
+      if (qb > w1) break;
+      step(q_lds0 + 2 * kTileElems, g_lds0 + 2 * kTileElems, row_lds + 3 * TB, q_lds0, g_lds0, row_lds);
     }
   }
   if (!klive) return;
