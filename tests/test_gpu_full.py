@@ -213,3 +213,47 @@ def test_packed_128k_window_subinstance():
     say("  window max-abs O {:.2e} LSE {:.2e} dQ {:.2e} dK {:.2e} dV {:.2e}".format(*errs))
     assert errs[0] <= TOL_O["bf16"] and errs[1] <= TOL_LSE
     assert max(errs[2:]) <= TOL_GRAD["bf16"]
+
+
+def test_packed_128k_closed_forms_all_rows():
+    """Full-size closed forms on every row and key of the packed 128K workload:
+    V = 1 gives O = 1 on every row (normalisation under random scores); Q = 0 gives uniform
+    weights over the visible keys, so dK = 0 exactly (it is a multiple of Q) and
+    dV_j = sum over later rows i of the segment of dO_i / n_i (n_i = keys row i sees), a
+    suffix sum; both checked on every key of two heads, LSE = ln n_i on every row."""
+    w = li.WORKLOADS["packed_128k_fwd_bwd"]
+    segs = li.workload_segments(w)
+    lengths = [n for _, n in segs]
+    bounds = li.segment_bounds(lengths)
+    say(f"{w.name}: closed forms on all rows (V = 1; Q = 0 forward + backward)")
+    seg_q, seg_k = li.workload_segment_ids(w)
+    sq, sk = seg_dev(seg_q), seg_dev(seg_k)
+    x = dev_inputs(w, ("q", "k", "do"))
+    ones = torch.ones((w.B, w.H, w.Sk, w.D), dtype=torch.bfloat16, device="cuda")
+    o1, _, _ = lwm.attention_forward(x["q"], x["k"], ones, sq, sk)
+    torch.cuda.synchronize()
+    err_one = float((o1.float() - 1.0).abs().max())
+    del o1, ones
+    v = li.device_normal((w.B, w.H, w.Sk, w.D), w.seed, w.value_scale, 2, torch.bfloat16, "cuda")
+    q0 = torch.zeros_like(x["q"])
+    o, lse, table = lwm.attention_forward(q0, x["k"], v, sq, sk)
+    dq, dk, dv = lwm.attention_backward(q0, x["k"], v, o, x["do"], lse, sq, sk, table)
+    torch.cuda.synchronize()
+    cnt = np.zeros(w.Sq)
+    for s, e in bounds:
+        cnt[s:e] = np.arange(1, e - s + 1)
+    err_lse = max_abs(f64(lse)[0], np.log(cnt)[None].repeat(w.H, 0))
+    err_dk = float(dk.float().abs().max())
+    err_dv = 0.0
+    for h in (0, w.H - 1):
+        dh = head_f64(x["do"], 0, h)
+        ref = np.empty_like(dh)
+        for s, e in bounds:
+            wsum = dh[s:e] / cnt[s:e, None]
+            ref[s:e] = np.cumsum(wsum[::-1], axis=0)[::-1]
+        err_dv = max(err_dv, max_abs(f64(dv[0, h]), ref))
+    say(f"  |O(V=1) - 1| {err_one:.2e}  LSE(Q=0) {err_lse:.2e}  |dK(Q=0)| {err_dk:.2e}  dV(Q=0) {err_dv:.2e}")
+    assert err_one <= TOL_O["bf16"]
+    assert err_lse <= TOL_LSE
+    assert err_dk == 0.0
+    assert err_dv <= TOL_GRAD["bf16"]
