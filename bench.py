@@ -112,8 +112,33 @@ def cpu_baseline(x_dev, lengths, scale, D, budget_s: float):
                   f"{W}-token window at segment start {s0} of the same 131072-token packed "
                   f"layout, {heads_done} head(s), {elapsed:.1f} s; unmasked FLOPs (14*D per "
                   f"visible pair) / wall time",
-        "cpu": platform.processor() or platform.machine(),
+        "cpu": cpu_model(),
+        "blas": blas_name(),
+        "host_cores_visible": len(os.sched_getaffinity(0)),
     }
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def blas_name() -> str:
+    try:
+        import numpy  # noqa: F401  (loads the BLAS threadpoolctl reports)
+        import threadpoolctl
+
+        for i in threadpoolctl.threadpool_info():
+            if i.get("user_api") == "blas":
+                return f"{i.get('internal_api')} {i.get('version')}"
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        pass
+    return "unknown"
 
 
 def main() -> int:
