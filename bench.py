@@ -141,6 +141,39 @@ def blas_name() -> str:
     return "unknown"
 
 
+def decode_parts(lwm, li, torch, reps: int):
+    """Split-KV decode against a 1M-token cache (one and sixteen new rows per head): the
+    path streams K and V once, so it is priced against HBM bandwidth.  The unsplit forward
+    on the same inputs is timed once beside it."""
+    out = {}
+    for name in ("decode_1m_q1", "decode_1m_q16"):
+        w = li.WORKLOADS[name]
+        seg_q, seg_k = li.workload_segment_ids(w)
+        q = li.device_normal((w.B, w.H, w.Sq, w.D), w.seed, w.value_scale, 0, torch.bfloat16, "cuda")
+        k = li.device_normal((w.B, w.H, w.Sk, w.D), w.seed, w.value_scale, 1, torch.bfloat16, "cuda")
+        v = li.device_normal((w.B, w.H, w.Sk, w.D), w.seed, w.value_scale, 2, torch.bfloat16, "cuda")
+        sq = torch.from_numpy(seg_q).cuda()
+        sk = torch.from_numpy(seg_k).cuda()
+        desc = lwm.make_desc(w.B, w.H, w.Sq, w.Sk, w.D, torch.bfloat16, q_offset=w.q_offset)
+        table = lwm.lwm_attn_build_block_table(desc, sq, sk)
+        ws = torch.empty(lwm.lwm_attn_decode_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device="cuda")
+        ms = time_events(lambda: lwm.lwm_attn_decode(desc, q, k, v, sq, sk, table, o, lse, ws), reps)
+        ms_unsplit = time_events(lambda: lwm.lwm_attn_fwd(desc, lwm.LWM_OUT_FINAL, q, k, v, sq, sk,
+                                                          table, o=o, lse=lse), 1)
+        # algorithmic bytes: K and V once, Q and O once, LSE
+        algo = 2 * w.B * w.H * w.Sk * w.D * 2 + 2 * w.B * w.H * w.Sq * w.D * 2 + 4 * w.B * w.H * w.Sq
+        gbs = algo / (ms * 1e-3) / 1e9
+        out[name] = {"ms": ms, "algo_bytes": algo, "gbs": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS,
+                     "workspace_bytes": ws.numel(), "unsplit_fwd_ms": ms_unsplit,
+                     "B": w.B, "H": w.H, "Sq": w.Sq, "Sk": w.Sk, "q_offset": w.q_offset}
+        print(f"[bench] {name}: {ms:.3f} ms, {gbs:.0f} GB/s (unsplit forward {ms_unsplit:.2f} ms)",
+              file=sys.stderr, flush=True)
+        del q, k, v, o, lse, ws, table
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,6 +183,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parts", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the split-KV decode parts (1M-token cache)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy three times (HBM counter calibration)")
     args = ap.parse_args()
@@ -259,6 +294,10 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x, lengths, w.scale, w.D, args.cpu_seconds)
+
+    if not args.no_parts and not args.no_decode:
+        del x, o, lse, dq, dk, dv, ws, table
+        parts.update(decode_parts(lwm, li, torch, args.part_reps))
 
     fwd_tflops = parts["fwd"]["tflops"] if parts else None
     bwd_ms = sum(parts[k]["ms"] for k in ("bwd_delta", "bwd_dq", "bwd_dkv")) if parts else None

@@ -125,6 +125,30 @@ int lwm_attn_merge_chunk(int64_t rows, int32_t D, float* m, float* l, float* acc
                          int32_t out_dtype, void* o, float* lse, void* stream);
 
 /*
+ * Decode: the FINAL forward for a few query rows (new tokens) against a long key/value
+ * cache, the inference side of the pages' million-token model (deep dive, section
+ * "RingAttention 为什么必要": 1M-token inference needs a v4-128 slice; section "局限与风险":
+ * inference cost).  Same result as lwm_attn_fwd(FINAL) on the same arguments, up to the
+ * order of float32 rounding; what differs is how the work is spread: the key tiles are cut
+ * into slices, every (query tile, head, slice) is one workgroup writing a partial state
+ * (m, l, acc) into the workspace, and one combine pass merges the slices exactly and
+ * normalises.  So few rows (Sq = 1 .. 128 per head) still fill the GPU and stream the cache
+ * at memory bandwidth; any Sq is accepted.  For new tokens at the end of a cache of Sk keys,
+ * pass causal = 1 and q_offset = k_offset + Sk - Sq.
+ *   o [B,H,Sq,D] bf16 and lse float32 [B,H,Sq] as for lwm_attn_fwd FINAL.
+ *   workspace: device memory of at least lwm_attn_decode_workspace_bytes(desc) bytes, owned
+ *   by the caller, contents on entry irrelevant (about nsplit * B*H*Sq * (D+2) * 4 bytes; a
+ *   few MiB for one token per head against a 1M-token cache).
+ * Supported: dtype LWM_BF16 with D = 128 (LWM_ERR_UNSUPPORTED otherwise), table built with
+ * block_q = block_k = 64.  The workspace size query returns 0 for a desc that is invalid or
+ * not supported.
+ */
+size_t lwm_attn_decode_workspace_bytes(const lwm_attn_desc* desc);
+int lwm_attn_decode(const lwm_attn_desc* desc, const void* q, const void* k, const void* v,
+                    const int32_t* seg_q, const int32_t* seg_k, const void* table, void* o,
+                    float* lse, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Backward of the forward above for an upstream gradient dO, recomputing P from the saved
  * LSE (P_ij = exp(s_ij - LSE_i) on visible pairs):
  *   Delta_i = <dO_i, O_i>,  dS_ij = P_ij (<dO_i, v_j> - Delta_i),

@@ -11,6 +11,7 @@ Convenience layers on top of those calls:
   attention_forward / attention_backward -- table + forward (+ backward) for one sequence
   ring_share_forward                      -- one device's share of the LWM ring: a query
                                              chunk merged against KV chunks in ring order
+  attention_decode                        -- few query rows against a long KV cache
 """
 from __future__ import annotations
 
@@ -36,6 +37,7 @@ EXPORTED = (
     "lwm_attn_block_table_bytes", "lwm_attn_build_block_table", "lwm_attn_fwd",
     "lwm_attn_merge_chunk", "lwm_attn_bwd_workspace_bytes", "lwm_attn_bwd",
     "lwm_attn_bwd_phase", "lwm_attn_status_string", "lwm_attn_version",
+    "lwm_attn_decode_workspace_bytes", "lwm_attn_decode",
 )
 LWM_BWD_DELTA, LWM_BWD_DQ, LWM_BWD_DKV = 0, 1, 2
 
@@ -77,6 +79,8 @@ def load_library(path: str = LIB_PATH):
         "lwm_attn_bwd_workspace_bytes": (SZ, [DP]),
         "lwm_attn_bwd": (ctypes.c_int, [DP, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "lwm_attn_bwd_phase": (ctypes.c_int, [DP, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "lwm_attn_decode_workspace_bytes": (SZ, [DP]),
+        "lwm_attn_decode": (ctypes.c_int, [DP, P, P, P, P, P, P, P, P, P, SZ, P]),
         "lwm_attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "lwm_attn_version": (ctypes.c_int, []),
     }
@@ -168,6 +172,18 @@ def lwm_attn_merge_chunk(rows: int, D: int, m, l, acc, mc=None, lc=None, accc=No
     _check("lwm_attn_merge_chunk", rc)
 
 
+def lwm_attn_decode_workspace_bytes(desc: Desc) -> int:
+    return int(load_library().lwm_attn_decode_workspace_bytes(ctypes.byref(desc)))
+
+
+def lwm_attn_decode(desc: Desc, q, k, v, seg_q, seg_k, table, o, lse, workspace, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load_library().lwm_attn_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                        _ptr(seg_q), _ptr(seg_k), _ptr(table), _ptr(o), _ptr(lse),
+                                        _ptr(workspace), ws_bytes, _stream(stream))
+    _check("lwm_attn_decode", rc)
+
+
 def lwm_attn_bwd_workspace_bytes(desc: Desc) -> int:
     return int(load_library().lwm_attn_bwd_workspace_bytes(ctypes.byref(desc)))
 
@@ -214,6 +230,26 @@ def attention_forward(q, k, v, seg_q, seg_k, *, scale=None, causal=True, q_offse
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     lwm_attn_fwd(desc, LWM_OUT_FINAL, q, k, v, seg_q, seg_k, table, o=o, lse=lse, stream=stream)
+    return o, lse, table
+
+
+def attention_decode(q, k, v, seg_q, seg_k, *, scale=None, causal=True, q_offset=None,
+                     k_offset=0, table=None, workspace=None, stream=None):
+    """(O, LSE, table) for a few query rows against a long KV cache by split-KV decode.
+    By default the queries are the cache's last Sq positions (q_offset = k_offset + Sk - Sq)."""
+    import torch
+
+    if q_offset is None:
+        q_offset = k_offset + k.shape[2] - q.shape[2]
+    desc = _desc_for(q, k, scale=scale, causal=causal, q_offset=q_offset, k_offset=k_offset)
+    if table is None:
+        table = lwm_attn_build_block_table(desc, seg_q, seg_k, stream=stream)
+    if workspace is None:
+        workspace = torch.empty(max(lwm_attn_decode_workspace_bytes(desc), 16), dtype=torch.uint8,
+                                device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    lwm_attn_decode(desc, q, k, v, seg_q, seg_k, table, o, lse, workspace, stream=stream)
     return o, lse, table
 
 

@@ -62,7 +62,7 @@ const char* lwm_attn_status_string(int status) {
   }
 }
 
-int lwm_attn_version(void) { return 100; }
+int lwm_attn_version(void) { return 200; }
 
 size_t lwm_attn_block_table_bytes(const lwm_attn_desc* d) {
   if (check_desc(d) != LWM_OK) return 0;
@@ -105,6 +105,28 @@ int lwm_attn_fwd(const lwm_attn_desc* d, int32_t mode, const void* q, const void
                             static_cast<const float*>(v), seg_q, seg_k, table,
                             static_cast<float*>(o), lse, m, l, acc, s);
   return hip_status(e);
+}
+
+size_t lwm_attn_decode_workspace_bytes(const lwm_attn_desc* d) {
+  if (check_attention_desc(d) != LWM_OK || d->dtype != LWM_BF16) return 0;
+  return lwm::decode_layout(*d).total;
+}
+
+int lwm_attn_decode(const lwm_attn_desc* d, const void* q, const void* k, const void* v,
+                    const int32_t* seg_q, const int32_t* seg_k, const void* table, void* o,
+                    float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  int rc = check_attention_desc(d);
+  if (rc) return rc;
+  if (d->dtype != LWM_BF16) return LWM_ERR_UNSUPPORTED;
+  if (d->Sq == 0) return LWM_OK;
+  if (!q || !seg_q || !table || !o || !lse) return LWM_ERR_INVALID_ARG;
+  if (d->Sk > 0 && (!k || !v || !seg_k)) return LWM_ERR_INVALID_ARG;
+  if (!workspace || ws_bytes < lwm_attn_decode_workspace_bytes(d)) return LWM_ERR_WORKSPACE;
+  const void* ptrs[] = {q, k, v, seg_q, seg_k, table, o, lse, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return LWM_ERR_ALIGNMENT;
+  return hip_status(lwm::launch_decode_bf16(*d, q, k, v, seg_q, seg_k, table, o, lse, workspace,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 int lwm_attn_merge_chunk(int64_t rows, int32_t D, float* m, float* l, float* acc, const float* mc,

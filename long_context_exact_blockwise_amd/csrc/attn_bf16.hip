@@ -201,8 +201,13 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // forward
 // ---------------------------------------------------------------------------------------
 
+// kSplit (decode): blockIdx.y selects a slice of split_tiles key tiles; the workgroup's
+// PARTIAL state for that slice goes to slice blockIdx.y of (Mo, Lo, ACC), each slice holding
+// B*H*Sq rows; waves whose 32 query rows all lie past Sq only help load tiles.
+template <bool kSplit>
 __global__ void __launch_bounds__(NT, 2)
-fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __restrict__ Q,
+fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, int split_tiles,
+                const uint16_t* __restrict__ Q,
                 const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                 const int32_t* __restrict__ seg_q, const int32_t* __restrict__ seg_k,
                 uint16_t* __restrict__ O, float* __restrict__ LSE, float* __restrict__ Mo,
@@ -245,6 +250,12 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
   const int32_t* rg0 = t.q_range + (int64_t(b) * t.nqb + r0) * 2;
   int lo, hi;
   range_union(rg0, rg0 + 2, has_r1, lo, hi);
+  if (kSplit) {
+    const int s0 = int(blockIdx.y) * split_tiles;
+    lo = max(lo, s0);
+    hi = min(hi, s0 + split_tiles - 1);
+  }
+  const bool wave_live = !kSplit || uniform(qt * BQ + wave * 32) < p.Sq;
   const uint8_t* st0 = t.status + (int64_t(b) * t.nqb + r0) * t.nkb;
   const uint8_t* st1 = st0 + t.nkb;
 
@@ -270,6 +281,10 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
     wait_vmem();
     __syncthreads();
     if (kn <= c1) issue(kn, kn_lds, vn_lds, sn_lds);
+    if (!wave_live) {
+      kt = kn;
+      return;
+    }
 
     // S^T = K Q^T for two 32-key blocks (K rows loaded in kperm order).  The operand reads
     // run four MFMAs ahead so LDS latency hides behind the matrix pipe.
@@ -373,8 +388,8 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
 
   const float l_tot = half_sum(l_run);
   if (!qlive) return;
-  const int64_t r64 = bh * p.Sq + qrow;
-  if (mode == LWM_OUT_FINAL) {
+  const int64_t r64 = (kSplit ? int64_t(blockIdx.y) * p.B * p.H * p.Sq : 0) + bh * p.Sq + qrow;
+  if (!kSplit && mode == LWM_OUT_FINAL) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* orow = O + r64 * D;
 #pragma unroll
@@ -402,6 +417,76 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
       Mo[r64] = l_tot > 0.f ? m_run * kLn2 : -INFINITY;
       Lo[r64] = l_tot;
     }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// split-KV decode: combine of the per-slice states
+// ---------------------------------------------------------------------------------------
+
+// Weight e^(x - m) of a slice whose max is x, where m >= x is the combined max; an empty
+// slice (x = -inf) weighs 0, also when every slice is empty (m = -inf).
+__device__ __forceinline__ float slice_weight(float x, float m) {
+  return x == -INFINITY ? 0.f : expf(x - m);
+}
+
+// Exact combine of nsplit partial states per row (the ring's merge applied to all slices
+// at once): m = max_s m_s, l = sum_s l_s e^(m_s - m), acc = sum_s acc_s e^(m_s - m), then
+// O = acc / l (bf16) and LSE = m + ln l, or O = 0 and LSE = -inf when no slice saw a key.
+// A group of 32 lanes owns one row (4 floats per lane); `gpr` groups (1, 2, 4 or 8) share a
+// row, each summing every gpr-th slice, and their sums meet in LDS.  Every group first
+// finds the row's max itself, its 32 lanes reading 32 slices' m at a time.
+__global__ void __launch_bounds__(NT) decode_combine_kernel(int64_t rows, int nsplit, int gpr,
+                                                            const float* __restrict__ M,
+                                                            const float* __restrict__ L,
+                                                            const float* __restrict__ ACC,
+                                                            uint16_t* __restrict__ O,
+                                                            float* __restrict__ LSE) {
+  __shared__ float4 part_acc[NT / 32][32];
+  __shared__ float part_l[NT / 32];
+  const int tid = threadIdx.x, grp = tid >> 5, lane = tid & 31;
+  const int rpb = (NT / 32) / gpr;  // rows per workgroup
+  const int sub = grp % gpr;
+  const int64_t nrb = (rows + rpb - 1) / rpb;
+  for (int64_t rb = blockIdx.x; rb < nrb; rb += gridDim.x) {
+    const int64_t row = rb * rpb + grp / gpr;
+    const bool live = row < rows;
+    float m = -INFINITY, l = 0.f;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (live) {
+      for (int s = lane; s < nsplit; s += 32) m = fmaxf(m, M[int64_t(s) * rows + row]);
+#pragma unroll
+      for (int off = 16; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 32));
+      for (int s = sub; s < nsplit; s += gpr) {
+        const int64_t r = int64_t(s) * rows + row;
+        const float w = slice_weight(M[r], m);
+        const float4 x = reinterpret_cast<const float4*>(ACC + r * D)[lane];
+        l = fmaf(L[r], w, l);
+        a.x = fmaf(x.x, w, a.x);
+        a.y = fmaf(x.y, w, a.y);
+        a.z = fmaf(x.z, w, a.z);
+        a.w = fmaf(x.w, w, a.w);
+      }
+    }
+    part_acc[grp][lane] = a;
+    if (lane == 0) part_l[grp] = l;
+    __syncthreads();
+    if (live && sub == 0) {
+      for (int g = 1; g < gpr; ++g) {
+        const float4 x = part_acc[grp + g][lane];
+        a.x += x.x;
+        a.y += x.y;
+        a.z += x.z;
+        a.w += x.w;
+        l += part_l[grp + g];
+      }
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      __bf16 o4[4] = {(__bf16)(a.x * inv), (__bf16)(a.y * inv), (__bf16)(a.z * inv),
+                      (__bf16)(a.w * inv)};
+      reinterpret_cast<uint2*>(O + row * D)[lane] = *reinterpret_cast<uint2*>(o4);
+      if (lane == 0) LSE[row] = l > 0.f ? m + logf(l) : -INFINITY;
+    }
+    __syncthreads();
   }
 }
 
@@ -773,10 +858,38 @@ hipError_t launch_fwd_bf16(const lwm_attn_desc& d, int mode, const void* q, cons
   const TableView t = table_view(d, table);
   const int nqt = (d.Sq + BQ - 1) / BQ;
   const int64_t grid = int64_t(nqt) * d.H * d.B;
-  fwd_bf16_kernel<<<dim3(unsigned(grid)), dim3(NT), 0, stream>>>(
-      attn_params(d), t, mode, nqt, static_cast<const uint16_t*>(q),
+  fwd_bf16_kernel<false><<<dim3(unsigned(grid)), dim3(NT), 0, stream>>>(
+      attn_params(d), t, mode, nqt, 0, static_cast<const uint16_t*>(q),
       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), seg_q, seg_k,
       static_cast<uint16_t*>(o), lse, m, l, acc);
+  return hipGetLastError();
+}
+
+// Split-KV decode: the forward in PARTIAL form with grid (query tiles x heads x batch,
+// slices), then the combine.  Workspace layout: decode_layout.
+hipError_t launch_decode_bf16(const lwm_attn_desc& d, const void* q, const void* k, const void* v,
+                              const int32_t* seg_q, const int32_t* seg_k, const void* table,
+                              void* o, float* lse, void* workspace, hipStream_t stream) {
+  const TableView t = table_view(d, table);
+  const DecodeLayout L = decode_layout(d);
+  char* ws = static_cast<char*>(workspace);
+  float* m = reinterpret_cast<float*>(ws + L.m_off);
+  float* l = reinterpret_cast<float*>(ws + L.l_off);
+  float* acc = reinterpret_cast<float*>(ws + L.acc_off);
+  const int nqt = (d.Sq + BQ - 1) / BQ;
+  const int64_t grid = int64_t(nqt) * d.H * d.B;
+  fwd_bf16_kernel<true><<<dim3(unsigned(grid), unsigned(L.nsplit)), dim3(NT), 0, stream>>>(
+      attn_params(d), t, LWM_OUT_PARTIAL, nqt, int(L.split_tiles), static_cast<const uint16_t*>(q),
+      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), seg_q, seg_k, nullptr,
+      nullptr, m, l, acc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t rows = int64_t(d.B) * d.H * d.Sq;
+  const int gpr = L.nsplit >= 8 ? 8 : L.nsplit >= 4 ? 4 : L.nsplit >= 2 ? 2 : 1;
+  const int64_t nrb = (rows + (NT / 32) / gpr - 1) / ((NT / 32) / gpr);
+  const unsigned cgrid = unsigned(nrb < (int64_t(1) << 20) ? nrb : (int64_t(1) << 20));
+  decode_combine_kernel<<<dim3(cgrid), dim3(NT), 0, stream>>>(
+      rows, int(L.nsplit), gpr, m, l, acc, static_cast<uint16_t*>(o), lse);
   return hipGetLastError();
 }
 

@@ -59,6 +59,38 @@ inline AttnParams attn_params(const lwm_attn_desc& d) {
   return AttnParams{d.B, d.H, d.Sq, d.Sk, d.q_offset, d.k_offset, d.scale, d.causal};
 }
 
+// Split-KV decode (bf16 path): the key tiles are cut into nsplit slices of split_tiles
+// 64-key tiles so that few query rows still fill the chip with about kDecodeGroups
+// workgroups; each slice's state (m, l, acc) for every query row lands in the workspace:
+// m [nsplit][rows], l [nsplit][rows], acc [nsplit][rows][D] float32, rows = B*H*Sq, each
+// part on a 256-byte boundary.  Slices never go below kDecodeMinTiles tiles, and there are
+// at most 65535 of them (the grid's y extent).
+constexpr int64_t kDecodeGroups = 8192;
+constexpr int64_t kDecodeMinTiles = 16;
+
+struct DecodeLayout {
+  int64_t split_tiles, nsplit;
+  size_t m_off, l_off, acc_off, total;
+};
+
+inline DecodeLayout decode_layout(const lwm_attn_desc& d) {
+  const int64_t nkt = (int64_t(d.Sk) + 63) / 64;
+  const int64_t base = (int64_t(d.Sq) + 127) / 128 * d.H * d.B;
+  const int64_t want = base > 0 ? (kDecodeGroups + base - 1) / base : 1;
+  int64_t st = (nkt + want - 1) / want;
+  if (st < kDecodeMinTiles) st = kDecodeMinTiles;
+  if (st < (nkt + 65534) / 65535) st = (nkt + 65534) / 65535;
+  DecodeLayout L;
+  L.split_tiles = st;
+  L.nsplit = nkt > 0 ? (nkt + st - 1) / st : 1;
+  const size_t rows = size_t(d.B) * d.H * d.Sq;
+  L.m_off = 0;
+  L.l_off = align256(size_t(L.nsplit) * rows * sizeof(float));
+  L.acc_off = L.l_off + align256(size_t(L.nsplit) * rows * sizeof(float));
+  L.total = L.acc_off + align256(size_t(L.nsplit) * rows * d.D * sizeof(float));
+  return L;
+}
+
 // ---- launchers (each returns the launch status) ----------------------------------------
 
 // Zero `bytes` (a multiple of 16) at a 16-byte aligned device address.
@@ -82,6 +114,10 @@ hipError_t launch_fwd_bf16(const lwm_attn_desc& d, int mode, const void* q, cons
                            const void* v, const int32_t* seg_q, const int32_t* seg_k,
                            const void* table, void* o, float* lse, float* m, float* l,
                            float* acc, hipStream_t stream);
+
+hipError_t launch_decode_bf16(const lwm_attn_desc& d, const void* q, const void* k, const void* v,
+                              const int32_t* seg_q, const int32_t* seg_k, const void* table,
+                              void* o, float* lse, void* workspace, hipStream_t stream);
 
 hipError_t launch_bwd_bf16(const lwm_attn_desc& d, int phase, const void* q, const void* k, const void* v,
                            const void* o, const void* dO, const float* lse,

@@ -65,6 +65,12 @@ WORKLOADS = {
     "packed_128k_fwd_bwd": Workload("packed_128k_fwd_bwd", 1, 32, 128, 131072, 131072, "bf16", 5,
                                     "packed", backward=True, sample_heads=4,
                                     sample_rows_per_head=64),
+    # decode: the newest tokens of one sequence against its 1M-token key/value cache (the
+    # pages' 1M-token inference), one token per step and a block of 16 rows
+    "decode_1m_q1": Workload("decode_1m_q1", 1, 32, 128, 1, 1 << 20, "bf16", 6, "single",
+                             q_offset=(1 << 20) - 1, sample_heads=8, sample_rows_per_head=1),
+    "decode_1m_q16": Workload("decode_1m_q16", 1, 32, 128, 16, 1 << 20, "bf16", 7, "single",
+                              q_offset=(1 << 20) - 16, sample_heads=4, sample_rows_per_head=16),
 }
 
 

@@ -155,3 +155,45 @@ def test_bwd_phase_rejects_bad_phase(lib):
     assert f(ctypes.byref(desc()), 3, *args, FAKE, 1 << 30, None) == INVALID
     assert f(ctypes.byref(desc()), -1, *args, FAKE, 1 << 30, None) == INVALID
     assert f(ctypes.byref(desc(D=64)), 1, *args, FAKE, 1 << 30, None) == UNSUP
+
+
+def test_decode_workspace_size(lib):
+    def al(x):
+        return (x + 255) // 256 * 256
+
+    # one new token per head against a 1M-token cache: the slices' states take a few MiB
+    for (H, Sq, Sk) in [(32, 1, 1 << 20), (32, 16, 1 << 20), (8, 4, 5000), (2, 300, 777), (1, 1, 0)]:
+        n = lwm.lwm_attn_decode_workspace_bytes(desc(H=H, Sq=Sq, Sk=Sk))
+        rows = H * Sq
+        # layout m [ns][rows], l [ns][rows], acc [ns][rows][128] for some slice count ns
+        ns = [s for s in range(1, 65536) if 2 * al(s * rows * 4) + al(s * rows * 512) == n]
+        assert ns, (H, Sq, Sk, n)
+        ntiles = -(-Sk // 64)
+        assert ns[0] <= max(1, ntiles)
+        if Sk == 1 << 20:
+            assert ns[0] >= 64
+            assert n < (8 << 20 if Sq == 1 else 128 << 20)
+    assert lwm.lwm_attn_decode_workspace_bytes(desc(dtype=lwm.LWM_F32, D=64)) == 0
+    assert lwm.lwm_attn_decode_workspace_bytes(desc(block_q=32)) == 0
+    assert lwm.lwm_attn_decode_workspace_bytes(desc(Sq=0)) == 0
+
+
+def test_decode_rejects_bad_arguments(lib):
+    f = lib.lwm_attn_decode
+
+    def call(d, ws=FAKE, ws_bytes=1 << 30, **kw):
+        names = ("q", "k", "v", "sq", "sk", "t", "o", "lse")
+        return f(ctypes.byref(d), *[kw.get(n, FAKE) for n in names], ws, ws_bytes, None)
+
+    assert call(desc(D=64, dtype=lwm.LWM_F32)) == UNSUP
+    assert call(desc(D=64)) == UNSUP
+    assert call(desc(block_k=32)) == UNSUP
+    assert call(desc(scale=0.0)) == INVALID
+    assert call(desc(), o=None) == INVALID
+    assert call(desc(), t=None) == INVALID
+    assert call(desc(), ws=None) == WS
+    assert call(desc(), ws_bytes=lwm.lwm_attn_decode_workspace_bytes(desc()) - 1) == WS
+    assert call(desc(), v=FAKE + 8) == ALIGN
+    assert call(desc(), ws=FAKE + 4) == ALIGN
+    assert call(desc(Sq=0), q=None, k=None, v=None, sq=None, sk=None, t=None, o=None, lse=None,
+                ws=None, ws_bytes=0) == OK
