@@ -205,13 +205,15 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // PARTIAL state for that slice goes to slice blockIdx.y of (Mo, Lo, ACC), each slice holding
 // B*H*Sq rows; waves whose 32 query rows all lie past Sq only help load tiles.
 template <bool kSplit>
-__global__ void __launch_bounds__(NT, 2)
-fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, int split_tiles,
-                const uint16_t* __restrict__ Q,
-                const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-                const int32_t* __restrict__ seg_q, const int32_t* __restrict__ seg_k,
-                uint16_t* __restrict__ O, float* __restrict__ LSE, float* __restrict__ Mo,
-                float* __restrict__ Lo, float* __restrict__ ACC) {
+__device__ __forceinline__ void fwd_bf16_body(AttnParams p, TableView t, int mode, int nqt,
+                                              int split_tiles, const uint16_t* __restrict__ Q,
+                                              const uint16_t* __restrict__ K,
+                                              const uint16_t* __restrict__ V,
+                                              const int32_t* __restrict__ seg_q,
+                                              const int32_t* __restrict__ seg_k,
+                                              uint16_t* __restrict__ O, float* __restrict__ LSE,
+                                              float* __restrict__ Mo, float* __restrict__ Lo,
+                                              float* __restrict__ ACC) {
   // double buffers: half 0 and half 1 of each array
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2 * kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2 * kTileElems];
@@ -420,9 +422,28 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, int split_tiles,
   }
 }
 
+__global__ void __launch_bounds__(NT, 2)
+fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __restrict__ Q,
+                const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                const int32_t* __restrict__ seg_q, const int32_t* __restrict__ seg_k,
+                uint16_t* __restrict__ O, float* __restrict__ LSE, float* __restrict__ Mo,
+                float* __restrict__ Lo, float* __restrict__ ACC) {
+  fwd_bf16_body<false>(p, t, mode, nqt, 0, Q, K, V, seg_q, seg_k, O, LSE, Mo, Lo, ACC);
+}
+
 // ---------------------------------------------------------------------------------------
-// split-KV decode: combine of the per-slice states
+// split-KV decode: the forward per key slice, then the combine of the per-slice states
 // ---------------------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(NT, 2)
+decode_bf16_kernel(AttnParams p, TableView t, int nqt, int split_tiles,
+                   const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                   const uint16_t* __restrict__ V, const int32_t* __restrict__ seg_q,
+                   const int32_t* __restrict__ seg_k, float* __restrict__ Mo,
+                   float* __restrict__ Lo, float* __restrict__ ACC) {
+  fwd_bf16_body<true>(p, t, LWM_OUT_PARTIAL, nqt, split_tiles, Q, K, V, seg_q, seg_k, nullptr,
+                      nullptr, Mo, Lo, ACC);
+}
 
 // Weight e^(x - m) of a slice whose max is x, where m >= x is the combined max; an empty
 // slice (x = -inf) weighs 0, also when every slice is empty (m = -inf).
@@ -858,8 +879,8 @@ hipError_t launch_fwd_bf16(const lwm_attn_desc& d, int mode, const void* q, cons
   const TableView t = table_view(d, table);
   const int nqt = (d.Sq + BQ - 1) / BQ;
   const int64_t grid = int64_t(nqt) * d.H * d.B;
-  fwd_bf16_kernel<false><<<dim3(unsigned(grid)), dim3(NT), 0, stream>>>(
-      attn_params(d), t, mode, nqt, 0, static_cast<const uint16_t*>(q),
+  fwd_bf16_kernel<<<dim3(unsigned(grid)), dim3(NT), 0, stream>>>(
+      attn_params(d), t, mode, nqt, static_cast<const uint16_t*>(q),
       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), seg_q, seg_k,
       static_cast<uint16_t*>(o), lse, m, l, acc);
   return hipGetLastError();
@@ -878,10 +899,9 @@ hipError_t launch_decode_bf16(const lwm_attn_desc& d, const void* q, const void*
   float* acc = reinterpret_cast<float*>(ws + L.acc_off);
   const int nqt = (d.Sq + BQ - 1) / BQ;
   const int64_t grid = int64_t(nqt) * d.H * d.B;
-  fwd_bf16_kernel<true><<<dim3(unsigned(grid), unsigned(L.nsplit)), dim3(NT), 0, stream>>>(
-      attn_params(d), t, LWM_OUT_PARTIAL, nqt, int(L.split_tiles), static_cast<const uint16_t*>(q),
-      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), seg_q, seg_k, nullptr,
-      nullptr, m, l, acc);
+  decode_bf16_kernel<<<dim3(unsigned(grid), unsigned(L.nsplit)), dim3(NT), 0, stream>>>(
+      attn_params(d), t, nqt, int(L.split_tiles), static_cast<const uint16_t*>(q),
+      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), seg_q, seg_k, m, l, acc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = int64_t(d.B) * d.H * d.Sq;
