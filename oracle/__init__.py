@@ -17,8 +17,10 @@ Modules:
                 merge, finalize, sampled rows)
   brute      -- pure-Python loops over tiny inputs, used to pin `attention`
   table      -- exact SKIP / PARTIAL / FULL classification of (query block, key block) pairs
+  rope       -- rotary position embedding with a large base theta, and attention on rotated
+                queries and keys
 """
-from . import attention, brute, table  # noqa: F401
+from . import attention, brute, rope, table  # noqa: F401
 from .attention import (  # noqa: F401
     visibility, forward, backward, forward_head, backward_head, partial_state, merge_states,
     finalize_state, forward_rows, dq_rows, EMPTY_M,

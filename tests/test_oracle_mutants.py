@@ -12,7 +12,9 @@ import pytest
 sys.path.insert(0, os.path.dirname(__file__))
 
 from oracle import attention as A
+from oracle import rope as R
 import test_oracle_pins as pins
+import test_oracle_rope_pins as rpins
 
 _orig_visibility = A.visibility
 _orig_backward_head = A.backward_head
@@ -67,6 +69,71 @@ def fwd_lse_without_log(q, k, v, mask, scale):
     s = np.where(mask, scale * (q @ k.T), -np.inf)
     m = s.max(axis=1)
     return o, np.where(np.isfinite(lse), m + np.exp(lse - m), lse), p
+
+
+_orig_rotate = R.rotate
+_orig_rope_fwd = R.attention_forward
+
+
+def rope_rotate_half_pairs(x, positions, theta, inverse=False):
+    # pairs (x[i], x[i + D/2]) instead of (x[2i], x[2i+1])
+    x = np.asarray(x, np.float64)
+    h = x.shape[-1] // 2
+    perm = np.empty(x.shape[-1], np.int64)
+    perm[0::2], perm[1::2] = np.arange(h), np.arange(h, 2 * h)
+    inv = np.argsort(perm)
+    return _orig_rotate(x[..., perm], positions, theta, inverse)[..., inv]
+
+
+def rope_half_exponent(x, positions, theta, inverse=False):
+    # frequencies theta^(-i/D) instead of theta^(-2i/D)
+    return _orig_rotate(x, positions, float(theta) ** 0.5, inverse)
+
+
+def rope_sign_flip(x, positions, theta, inverse=False):
+    return _orig_rotate(x, positions, theta, not inverse)
+
+
+def rope_bwd_no_unrotate(q, k, v, do, seg_q, seg_k, scale, theta, causal=True, q_offset=0,
+                         k_offset=0):
+    qr = _orig_rotate(q, q_offset + np.arange(q.shape[-2]), theta)
+    kr = _orig_rotate(k, k_offset + np.arange(k.shape[-2]), theta)
+    return A.backward(qr, kr, v, do, seg_q, seg_k, scale, causal, q_offset, k_offset)
+
+
+def rope_fwd_local_key_positions(q, k, v, seg_q, seg_k, scale, theta, causal=True, q_offset=0,
+                                 k_offset=0):
+    qr = _orig_rotate(q, q_offset + np.arange(q.shape[-2]), theta)
+    kr = _orig_rotate(k, np.arange(k.shape[-2]), theta)
+    return A.forward(qr, kr, v, seg_q, seg_k, scale, causal, q_offset, k_offset)
+
+
+def rope_fwd_local_query_positions(q, k, v, seg_q, seg_k, scale, theta, causal=True, q_offset=0,
+                                   k_offset=0):
+    qr = _orig_rotate(q, np.arange(q.shape[-2]), theta)
+    kr = _orig_rotate(k, k_offset + np.arange(k.shape[-2]), theta)
+    return A.forward(qr, kr, v, seg_q, seg_k, scale, causal, q_offset, k_offset)
+
+
+ROPE_MUTANTS = [
+    ("rotate", rope_rotate_half_pairs, [rpins.test_rope_worked_example]),
+    ("rotate", rope_half_exponent, [rpins.test_rope_worked_example]),
+    ("rotate", rope_sign_flip, [rpins.test_rope_worked_example]),
+    ("attention_backward", rope_bwd_no_unrotate, [rpins.test_rope_attention_gradients_by_finite_differences]),
+    ("attention_forward", rope_fwd_local_key_positions,
+     [rpins.test_rope_attention_is_invariant_to_a_common_position_shift]),
+    ("attention_forward", rope_fwd_local_query_positions,
+     [rpins.test_rope_ring_chunks_with_global_key_positions_equal_full]),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(ROPE_MUTANTS)))
+def test_rope_pins_catch_mutant(idx, monkeypatch):
+    name, mutant, checks = ROPE_MUTANTS[idx]
+    monkeypatch.setattr(R, name, mutant)
+    for check in checks:
+        with pytest.raises(AssertionError):
+            check()
 
 
 MUTANTS = [
