@@ -279,6 +279,15 @@ def main() -> int:
                                      "gbs": merge_bytes / (ms_merge * 1e-3) / 1e9,
                                      "frac_hbm_peak": merge_bytes / (ms_merge * 1e-3) / 1e9 / PEAK_HBM_GBS}
         del st, accs
+        # RoPE of Q and K at theta = 10M (the pages' 128K stage), each read and written once
+        qr, kr = torch.empty_like(x["q"]), torch.empty_like(x["k"])
+        ms_rope = time_events(lambda: (lwm.lwm_attn_rope(x["q"], qr, 0, 1e7),
+                                       lwm.lwm_attn_rope(x["k"], kr, 0, 1e7)), reps)
+        rope_bytes = 2 * 2 * x["q"].numel() * 2
+        parts["rope_qk"] = {"ms": ms_rope, "algo_bytes": rope_bytes, "theta": 1e7,
+                            "gbs": rope_bytes / (ms_rope * 1e-3) / 1e9,
+                            "frac_hbm_peak": rope_bytes / (ms_rope * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        del qr, kr
         dom = max(("fwd", "bwd_dq", "bwd_dkv"), key=lambda k: parts[k]["ms"])
         traffic = None
         if os.path.exists(TRAFFIC_FILE):

@@ -181,6 +181,26 @@ int lwm_attn_bwd_phase(const lwm_attn_desc* desc, int32_t phase, const void* q, 
                        const int32_t* seg_q, const int32_t* seg_k, const void* table, void* dq,
                        void* dk, void* dv, void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * Rotary position embedding (RoPE) with a large base theta, the step before Q K^T in every
+ * layer of the LWM model: the pages extend the context by enlarging theta (deep dive, section
+ * "Stage I：长上下文语言模型" and Tables 11 and 13: 1M at 32K tokens, 10M at 128K and 256K, 25M at
+ * 512K, 50M at 1M).  The pages give no formula; the textbook rotary embedding is used: pair
+ * i = (x[2i], x[2i+1]) of the row of the token at position p turns by the angle
+ * p * theta^(-2i/D):
+ *   out[2i]   = x[2i] cos(a) - x[2i+1] sin(a),   out[2i+1] = x[2i] sin(a) + x[2i+1] cos(a).
+ * inverse = 1 turns by -a instead (the transpose: it carries dQ, dK of the rotated vectors
+ * back to the unrotated ones).  x and out are [B,H,S,D] (dtype LWM_BF16 or LWM_F32), row s
+ * at position pos_offset + s; use the attention desc's q_offset / k_offset so positions are
+ * global.  out may be x itself (in place) or a disjoint buffer.
+ * Angles are reduced to a fraction of a turn in float64 before float32 sin/cos, so the
+ * angle error stays below 1e-6 radian at every position; bf16 results are rounded to
+ * nearest even.  Requires D in {8, 16, 32, 64, 128, 256}, theta > 1 and finite,
+ * pos_offset >= 0, pos_offset + S <= 2^32.  B*H*S = 0 does nothing.
+ */
+int lwm_attn_rope(int32_t B, int32_t H, int32_t S, int32_t D, int32_t dtype, int64_t pos_offset,
+                  double theta, int32_t inverse, const void* x, void* out, void* stream);
+
 /* Static, NUL-terminated name of a status code. */
 const char* lwm_attn_status_string(int status);
 

@@ -12,6 +12,9 @@ Convenience layers on top of those calls:
   ring_share_forward                      -- one device's share of the LWM ring: a query
                                              chunk merged against KV chunks in ring order
   attention_decode                        -- few query rows against a long KV cache
+  rope                                    -- RoPE rotation of Q or K by global position
+                                             (also the rope_theta option of the forward and
+                                             backward layers)
 """
 from __future__ import annotations
 
@@ -37,7 +40,7 @@ EXPORTED = (
     "lwm_attn_block_table_bytes", "lwm_attn_build_block_table", "lwm_attn_fwd",
     "lwm_attn_merge_chunk", "lwm_attn_bwd_workspace_bytes", "lwm_attn_bwd",
     "lwm_attn_bwd_phase", "lwm_attn_status_string", "lwm_attn_version",
-    "lwm_attn_decode_workspace_bytes", "lwm_attn_decode",
+    "lwm_attn_decode_workspace_bytes", "lwm_attn_decode", "lwm_attn_rope",
 )
 LWM_BWD_DELTA, LWM_BWD_DQ, LWM_BWD_DKV = 0, 1, 2
 
@@ -81,6 +84,7 @@ def load_library(path: str = LIB_PATH):
         "lwm_attn_bwd_phase": (ctypes.c_int, [DP, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "lwm_attn_decode_workspace_bytes": (SZ, [DP]),
         "lwm_attn_decode": (ctypes.c_int, [DP, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "lwm_attn_rope": (ctypes.c_int, [I32, I32, I32, I32, I32, I64, ctypes.c_double, I32, P, P, P]),
         "lwm_attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "lwm_attn_version": (ctypes.c_int, []),
     }
@@ -184,6 +188,17 @@ def lwm_attn_decode(desc: Desc, q, k, v, seg_q, seg_k, table, o, lse, workspace,
     _check("lwm_attn_decode", rc)
 
 
+def lwm_attn_rope(x, out, pos_offset: int, theta: float, inverse: bool = False, stream=None):
+    """RoPE of x [B,H,S,D] (bf16 or float32) into out (may be x itself), row s at position
+    pos_offset + s."""
+    if x.dim() != 4 or out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError("lwm_attn_rope: x and out must be [B,H,S,D] of one shape and dtype")
+    B, H, S, D = x.shape
+    rc = load_library().lwm_attn_rope(B, H, S, D, _dtype_code(x.dtype), int(pos_offset), float(theta),
+                                      int(bool(inverse)), _ptr(x), _ptr(out), _stream(stream))
+    _check("lwm_attn_rope", rc)
+
+
 def lwm_attn_bwd_workspace_bytes(desc: Desc) -> int:
     return int(load_library().lwm_attn_bwd_workspace_bytes(ctypes.byref(desc)))
 
@@ -219,11 +234,28 @@ def _desc_for(q, k, *, scale, causal, q_offset, k_offset):
                      k_offset=k_offset)
 
 
-def attention_forward(q, k, v, seg_q, seg_k, *, scale=None, causal=True, q_offset=0, k_offset=0,
-                      table=None, stream=None):
-    """(O, LSE, table) for Q [B,H,Sq,D] against K, V [B,H,Sk,D] with segment ids."""
+def rope(x, pos_offset: int, theta: float, *, inverse: bool = False, out=None, stream=None):
+    """RoPE-rotated copy of x [B,H,S,D] (or into `out`, which may be x for in place)."""
     import torch
 
+    out = torch.empty_like(x) if out is None else out
+    lwm_attn_rope(x, out, pos_offset, theta, inverse, stream=stream)
+    return out
+
+
+def _rotated(q, k, rope_theta, q_offset, k_offset, stream):
+    if rope_theta is None:
+        return q, k
+    return (rope(q, q_offset, rope_theta, stream=stream), rope(k, k_offset, rope_theta, stream=stream))
+
+
+def attention_forward(q, k, v, seg_q, seg_k, *, scale=None, causal=True, q_offset=0, k_offset=0,
+                      table=None, rope_theta=None, stream=None):
+    """(O, LSE, table) for Q [B,H,Sq,D] against K, V [B,H,Sk,D] with segment ids.  With
+    rope_theta, Q and K are first rotated by RoPE at their global positions."""
+    import torch
+
+    q, k = _rotated(q, k, rope_theta, q_offset, k_offset, stream)
     desc = _desc_for(q, k, scale=scale, causal=causal, q_offset=q_offset, k_offset=k_offset)
     if table is None:
         table = lwm_attn_build_block_table(desc, seg_q, seg_k, stream=stream)
@@ -274,10 +306,12 @@ def attention_partial(q, k, v, seg_q, seg_k, *, scale=None, causal=True, q_offse
 
 
 def attention_backward(q, k, v, o, do, lse, seg_q, seg_k, table, *, scale=None, causal=True,
-                       q_offset=0, k_offset=0, workspace=None, stream=None):
-    """(dQ, dK, dV) by LSE recompute."""
+                       q_offset=0, k_offset=0, workspace=None, rope_theta=None, stream=None):
+    """(dQ, dK, dV) by LSE recompute.  With rope_theta, q and k are the unrotated inputs of a
+    RoPE forward: they are rotated again, and dQ, dK are rotated back (in place)."""
     import torch
 
+    q, k = _rotated(q, k, rope_theta, q_offset, k_offset, stream)
     desc = _desc_for(q, k, scale=scale, causal=causal, q_offset=q_offset, k_offset=k_offset)
     if workspace is None:
         workspace = torch.empty(max(lwm_attn_bwd_workspace_bytes(desc), 16), dtype=torch.uint8,
@@ -285,6 +319,9 @@ def attention_backward(q, k, v, o, do, lse, seg_q, seg_k, table, *, scale=None, 
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     lwm_attn_bwd(desc, q, k, v, o, do, lse, seg_q, seg_k, table, dq, dk, dv, workspace,
                  stream=stream)
+    if rope_theta is not None:
+        rope(dq, q_offset, rope_theta, inverse=True, out=dq, stream=stream)
+        rope(dk, k_offset, rope_theta, inverse=True, out=dk, stream=stream)
     return dq, dk, dv
 
 

@@ -150,6 +150,28 @@ int lwm_attn_merge_chunk(int64_t rows, int32_t D, float* m, float* l, float* acc
                                       lse, static_cast<hipStream_t>(stream)));
 }
 
+int lwm_attn_rope(int32_t B, int32_t H, int32_t S, int32_t D, int32_t dtype, int64_t pos_offset,
+                  double theta, int32_t inverse, const void* x, void* out, void* stream) {
+  if (dtype != LWM_BF16 && dtype != LWM_F32) return LWM_ERR_INVALID_ARG;
+  if (inverse != 0 && inverse != 1) return LWM_ERR_INVALID_ARG;
+  if (!(theta > 1.0) || theta == std::numeric_limits<double>::infinity()) return LWM_ERR_INVALID_ARG;
+  if (B < 0 || H < 0 || S < 0 || pos_offset < 0) return LWM_ERR_SHAPE;
+  if (!(D == 8 || D == 16 || D == 32 || D == 64 || D == 128 || D == 256)) return LWM_ERR_UNSUPPORTED;
+  if (pos_offset + int64_t(S) > (int64_t(1) << 32)) return LWM_ERR_SHAPE;
+  const int64_t rows = int64_t(B) * H * S;
+  if (rows > (int64_t(1) << 40) / D) return LWM_ERR_SHAPE;
+  if (rows == 0) return LWM_OK;
+  if (!x || !out) return LWM_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(out)) return LWM_ERR_ALIGNMENT;
+  // in place or disjoint; a partial overlap would let threads overwrite rows others read
+  const size_t bytes = size_t(rows) * D * (dtype == LWM_BF16 ? 2 : 4);
+  const char* xa = static_cast<const char*>(x);
+  const char* oa = static_cast<const char*>(out);
+  if (xa != oa && xa < oa + bytes && oa < xa + bytes) return LWM_ERR_INVALID_ARG;
+  return hip_status(lwm::launch_rope(B, H, S, D, dtype, pos_offset, theta, inverse, x, out,
+                                     static_cast<hipStream_t>(stream)));
+}
+
 size_t lwm_attn_bwd_workspace_bytes(const lwm_attn_desc* d) {
   if (check_desc(d) != LWM_OK) return 0;
   // Delta and LSE * log2(e), one float32 per query row each

@@ -124,6 +124,10 @@ hipError_t launch_bwd_bf16(const lwm_attn_desc& d, int phase, const void* q, con
                            const int32_t* seg_q, const int32_t* seg_k, const void* table,
                            void* dq, void* dk, void* dv, float* workspace, hipStream_t stream);
 
+// RoPE over rows = B*H*S rows of D elements (D in 8..256, a power of two), in place allowed.
+hipError_t launch_rope(int32_t B, int32_t H, int32_t S, int32_t D, int32_t dtype, int64_t pos0,
+                       double theta, int32_t inverse, const void* x, void* y, hipStream_t stream);
+
 hipError_t launch_merge(int64_t rows, int32_t D, float* m, float* l, float* acc, const float* mc,
                         const float* lc, const float* accc, int32_t finalize, int32_t out_dtype,
                         void* o, float* lse, hipStream_t stream);

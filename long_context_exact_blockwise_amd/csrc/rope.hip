@@ -1,0 +1,118 @@
+// Rotary position embedding (RoPE) with a large base theta: rotates a [B,H,S,D] tensor of
+// queries or keys by global token position, or rotates a gradient back (inverse).
+//
+// The LWM pages extend the context window by enlarging RoPE's base theta (deep dive, section
+// "Stage I：长上下文语言模型" and Tables 11 and 13: theta from 1M at 32K tokens up to 50M at 1M
+// tokens).  Pair i = (x[2i], x[2i+1]) of the token at position p turns by the angle
+// p * theta^(-2i/D); the inverse turns by the opposite angle.
+//
+// Precision.  At theta = 5e7 and p near 2^20 the angle of the fastest pair is about 10^6
+// radians; a float32 product p * w_i would already be off by several hundredths of a radian.
+// So the angle is formed in float64 as revolutions, t = p * w_i / (2 pi), whose fractional
+// part t - rint(t) is exact in float64; only that fraction in [-1/2, 1/2] goes to float32,
+// and sin/cos of (2 pi * fraction) come from sincospi.  The angle error stays below 1e-6
+// radian for every position below 2^32.
+//
+// Work split.  The kernel streams the tensor once (HBM bound).  A thread owns 8 consecutive
+// elements (4 pairs) of a row; a row of D elements takes D/8 threads, and the grid stride is
+// a multiple of D/8, so a thread meets the same 4 pairs in every row it visits and works out
+// their frequencies once.
+
+#include <cmath>
+
+#include "common.h"
+
+namespace lwm {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr double kInv2Pi = 0.15915494309189533577;
+
+__device__ __forceinline__ void load8(const uint16_t* p, float* v) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void store8(uint16_t* p, const float* v) {
+  __bf16 b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b[i] = (__bf16)v[i];  // round to nearest even
+  *reinterpret_cast<uint4*>(p) = *reinterpret_cast<const uint4*>(b);
+}
+__device__ __forceinline__ void load8(const float* p, float* v) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void store8(float* p, const float* v) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+rope_kernel(int64_t rows, int32_t S, int32_t D, int32_t tpr_shift, int64_t pos0, double log2_theta,
+            float dir, const T* x, T* y) {  // x and y may be the same buffer
+  // D / 8 = 2^tpr_shift threads per row, a divisor of kThreads
+  const int64_t total = rows << tpr_shift;
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  int64_t g = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  const int part = int(g & ((1 << tpr_shift) - 1));
+  // revolutions per position of this thread's pairs: theta^(-2i/D) / (2 pi)
+  double rev[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) rev[k] = exp2(-double(2 * (4 * part + k)) / D * log2_theta) * kInv2Pi;
+  // the row advances by a fixed step per iteration; its position within S is carried along
+  int64_t row = g >> tpr_shift;
+  const int64_t row_step = stride >> tpr_shift;
+  int64_t s = row % S;
+  const int64_t s_step = row_step % S;
+  for (; g < total; g += stride, row += row_step) {
+    const double pos = double(pos0 + s);
+    s += s_step;
+    if (s >= S) s -= S;
+    const int64_t off = row * D + 8 * part;
+    float v[8];
+    load8(x + off, v);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const double t = pos * rev[k];
+      const float f = float(t - rint(t));  // fraction of a turn, |f| <= 1/2
+      float sn, cs;
+      sincospif(2.f * f, &sn, &cs);
+      sn *= dir;
+      const float a = v[2 * k], b = v[2 * k + 1];
+      v[2 * k] = a * cs - b * sn;
+      v[2 * k + 1] = a * sn + b * cs;
+    }
+    store8(y + off, v);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rope(int32_t B, int32_t H, int32_t S, int32_t D, int32_t dtype, int64_t pos0,
+                       double theta, int32_t inverse, const void* x, void* y, hipStream_t stream) {
+  const int64_t rows = int64_t(B) * H * S;
+  const int64_t threads = rows * (D / 8);
+  int64_t blocks = (threads + kThreads - 1) / kThreads;
+  if (blocks > 65536) blocks = 65536;  // grid stride loop beyond that
+  const double l2t = std::log2(theta);
+  const float dir = inverse ? -1.f : 1.f;
+  int shift = 0;
+  while ((8 << shift) < D) ++shift;
+  if (dtype == LWM_BF16)
+    rope_kernel<uint16_t><<<dim3(unsigned(blocks)), dim3(kThreads), 0, stream>>>(
+        rows, S, D, shift, pos0, l2t, dir, static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y));
+  else
+    rope_kernel<float><<<dim3(unsigned(blocks)), dim3(kThreads), 0, stream>>>(
+        rows, S, D, shift, pos0, l2t, dir, static_cast<const float*>(x), static_cast<float*>(y));
+  return hipGetLastError();
+}
+
+}  // namespace lwm

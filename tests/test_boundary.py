@@ -197,3 +197,26 @@ def test_decode_rejects_bad_arguments(lib):
     assert call(desc(), ws=FAKE + 4) == ALIGN
     assert call(desc(Sq=0), q=None, k=None, v=None, sq=None, sk=None, t=None, o=None, lse=None,
                 ws=None, ws_bytes=0) == OK
+
+
+def test_rope_rejects_bad_arguments(lib):
+    f = lib.lwm_attn_rope
+
+    def call(B=1, H=2, S=100, D=128, dtype=lwm.LWM_BF16, pos=0, theta=1e6, inverse=0, x=FAKE,
+             out=FAKE):
+        return f(B, H, S, D, dtype, pos, theta, inverse, x, out, None)
+
+    assert call(D=96) == UNSUP
+    assert call(D=512) == UNSUP
+    assert call(dtype=7) == INVALID
+    assert call(inverse=2) == INVALID
+    assert call(theta=1.0) == INVALID
+    assert call(theta=float("nan")) == INVALID
+    assert call(theta=float("inf")) == INVALID
+    assert call(S=-1) == SHAPE
+    assert call(pos=-3) == SHAPE
+    assert call(pos=(1 << 32) - 99) == SHAPE          # last position 2^32 is out of range
+    assert call(x=None) == INVALID
+    assert call(out=FAKE + 8) == ALIGN
+    assert call(out=FAKE + 256) == INVALID           # partial overlap with x
+    assert call(S=0, x=None, out=None) == OK         # nothing to do
