@@ -14,9 +14,12 @@
 // radian for every position below 2^32.
 //
 // Work split.  The kernel streams the tensor once (HBM bound).  A thread owns 8 consecutive
-// elements (4 pairs) of a row; a row of D elements takes D/8 threads, and the grid stride is
-// a multiple of D/8, so a thread meets the same 4 pairs in every row it visits and works out
-// their frequencies once.
+// elements (4 pairs) at one position; a position's D elements take D/8 threads, and the grid
+// stride is a multiple of D/8, so a thread meets the same 4 pairs at every position it visits
+// and works out their frequencies once.  The angles of a position serve every batch row and
+// head, so a thread rotates its 8 elements in a group of (batch, head) rows of that position
+// (four rows' loads in flight at a time) after one sin/cos per pair; the grid's y index
+// picks the group.
 
 #include <cmath>
 
@@ -26,6 +29,10 @@ namespace lwm {
 namespace {
 
 constexpr int kThreads = 256;
+#ifndef LWM_ROPE_ROWS
+#define LWM_ROPE_ROWS 8
+#endif
+constexpr int64_t kRowsPerThread = LWM_ROPE_ROWS;  // (batch, head) rows per thread and position
 constexpr double kInv2Pi = 0.15915494309189533577;
 
 __device__ __forceinline__ void load8(const uint16_t* p, float* v) {
@@ -56,10 +63,10 @@ __device__ __forceinline__ void store8(float* p, const float* v) {
 
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
-rope_kernel(int64_t rows, int32_t S, int32_t D, int32_t tpr_shift, int64_t pos0, double log2_theta,
-            float dir, const T* x, T* y) {  // x and y may be the same buffer
-  // D / 8 = 2^tpr_shift threads per row, a divisor of kThreads
-  const int64_t total = rows << tpr_shift;
+rope_kernel(int64_t BH, int64_t rpt, int32_t S, int32_t D, int32_t tpr_shift, int64_t pos0,
+            double log2_theta, float dir, const T* x, T* y) {  // x and y may be the same buffer
+  // D / 8 = 2^tpr_shift threads per position, a divisor of kThreads
+  const int64_t total = int64_t(S) << tpr_shift;
   const int64_t stride = int64_t(gridDim.x) * kThreads;
   int64_t g = int64_t(blockIdx.x) * kThreads + threadIdx.x;
   const int part = int(g & ((1 << tpr_shift) - 1));
@@ -67,30 +74,53 @@ rope_kernel(int64_t rows, int32_t S, int32_t D, int32_t tpr_shift, int64_t pos0,
   double rev[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) rev[k] = exp2(-double(2 * (4 * part + k)) / D * log2_theta) * kInv2Pi;
-  // the row advances by a fixed step per iteration; its position within S is carried along
-  int64_t row = g >> tpr_shift;
-  const int64_t row_step = stride >> tpr_shift;
-  int64_t s = row % S;
-  const int64_t s_step = row_step % S;
-  for (; g < total; g += stride, row += row_step) {
+  const int64_t rstride = int64_t(S) * D;  // from one (batch, head) row block to the next
+  // this workgroup's share of the batch rows and heads: rpt of them
+  const int64_t bh0 = int64_t(blockIdx.y) * rpt;
+  if (bh0 >= BH) return;
+  const int64_t bh1 = bh0 + rpt < BH ? bh0 + rpt : BH;
+  x += bh0 * rstride;
+  y += bh0 * rstride;
+  for (; g < total; g += stride) {
+    const int64_t s = g >> tpr_shift;
     const double pos = double(pos0 + s);
-    s += s_step;
-    if (s >= S) s -= S;
-    const int64_t off = row * D + 8 * part;
-    float v[8];
-    load8(x + off, v);
+    float cs[4], sn[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const double t = pos * rev[k];
       const float f = float(t - rint(t));  // fraction of a turn, |f| <= 1/2
-      float sn, cs;
-      sincospif(2.f * f, &sn, &cs);
-      sn *= dir;
-      const float a = v[2 * k], b = v[2 * k + 1];
-      v[2 * k] = a * cs - b * sn;
-      v[2 * k + 1] = a * sn + b * cs;
+      sincospif(2.f * f, &sn[k], &cs[k]);
+      sn[k] *= dir;
     }
-    store8(y + off, v);
+    // every batch row and head shares the position, hence the angles
+    const T* xs = x + s * D + 8 * part;
+    T* ys = y + s * D + 8 * part;
+    auto turn = [&](float* v) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float a = v[2 * k], b = v[2 * k + 1];
+        v[2 * k] = a * cs[k] - b * sn[k];
+        v[2 * k + 1] = a * sn[k] + b * cs[k];
+      }
+    };
+    const int64_t n = bh1 - bh0;
+    int64_t bh = 0;
+    for (; bh + 4 <= n; bh += 4) {
+      float v[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) load8(xs + (bh + u) * rstride, v[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        turn(v[u]);
+        store8(ys + (bh + u) * rstride, v[u]);
+      }
+    }
+    for (; bh < n; ++bh) {
+      float v[8];
+      load8(xs + bh * rstride, v);
+      turn(v);
+      store8(ys + bh * rstride, v);
+    }
   }
 }
 
@@ -98,20 +128,25 @@ rope_kernel(int64_t rows, int32_t S, int32_t D, int32_t tpr_shift, int64_t pos0,
 
 hipError_t launch_rope(int32_t B, int32_t H, int32_t S, int32_t D, int32_t dtype, int64_t pos0,
                        double theta, int32_t inverse, const void* x, void* y, hipStream_t stream) {
-  const int64_t rows = int64_t(B) * H * S;
-  const int64_t threads = rows * (D / 8);
+  const int64_t threads = int64_t(S) * (D / 8);
   int64_t blocks = (threads + kThreads - 1) / kThreads;
   if (blocks > 65536) blocks = 65536;  // grid stride loop beyond that
+  const int64_t bh = int64_t(B) * H;
+  int64_t rpt = kRowsPerThread;
+  if ((bh + rpt - 1) / rpt > 65535) rpt = (bh + 65534) / 65535;  // the grid's y extent
+  const int64_t groups = (bh + rpt - 1) / rpt;
   const double l2t = std::log2(theta);
   const float dir = inverse ? -1.f : 1.f;
   int shift = 0;
   while ((8 << shift) < D) ++shift;
   if (dtype == LWM_BF16)
-    rope_kernel<uint16_t><<<dim3(unsigned(blocks)), dim3(kThreads), 0, stream>>>(
-        rows, S, D, shift, pos0, l2t, dir, static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y));
+    rope_kernel<uint16_t><<<dim3(unsigned(blocks), unsigned(groups)), dim3(kThreads), 0, stream>>>(
+        bh, rpt, S, D, shift, pos0, l2t, dir, static_cast<const uint16_t*>(x),
+        static_cast<uint16_t*>(y));
   else
-    rope_kernel<float><<<dim3(unsigned(blocks)), dim3(kThreads), 0, stream>>>(
-        rows, S, D, shift, pos0, l2t, dir, static_cast<const float*>(x), static_cast<float*>(y));
+    rope_kernel<float><<<dim3(unsigned(blocks), unsigned(groups)), dim3(kThreads), 0, stream>>>(
+        bh, rpt, S, D, shift, pos0, l2t, dir, static_cast<const float*>(x),
+        static_cast<float*>(y));
   return hipGetLastError();
 }
 
