@@ -19,8 +19,9 @@ Modules:
   table      -- exact SKIP / PARTIAL / FULL classification of (query block, key block) pairs
   rope       -- rotary position embedding with a large base theta, and attention on rotated
                 queries and keys
+  packed_loss -- next-token cross-entropy reweighted so every packed sample weighs the same
 """
-from . import attention, brute, rope, table  # noqa: F401
+from . import attention, brute, packed_loss, rope, table  # noqa: F401
 from .attention import (  # noqa: F401
     visibility, forward, backward, forward_head, backward_head, partial_state, merge_states,
     finalize_state, forward_rows, dq_rows, EMPTY_M,

@@ -136,6 +136,64 @@ def test_rope_pins_catch_mutant(idx, monkeypatch):
             check()
 
 
+from oracle import packed_loss as PL
+import test_oracle_loss_pins as lpins
+
+_orig_weights = PL.token_weights
+_orig_token_losses = PL.token_losses
+
+
+def weights_token_mean(targets, seg):
+    live = (np.asarray(seg) >= 0) & (np.asarray(targets) >= 0)
+    return live / max(1, live.sum())
+
+
+def weights_ids_shared_across_rows(targets, seg):
+    # N and n_s counted per id over the whole batch, as if rows shared their samples
+    seg = np.asarray(seg)
+    live = (seg >= 0) & (np.asarray(targets) >= 0)
+    ids, n = np.unique(seg[live], return_counts=True)
+    w = np.zeros(seg.shape)
+    for i, c in zip(ids, n):
+        w[(seg == i) & live] = 1.0 / (len(ids) * c)
+    return w
+
+
+def losses_without_max_shift(logits, targets):
+    x = np.asarray(logits, np.float64)
+    targets = np.asarray(targets)
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        lse = np.log(np.exp(x).sum(axis=-1))
+    y = np.where(targets >= 0, targets, 0)
+    picked = np.take_along_axis(x, y[..., None], axis=-1)[..., 0]
+    return np.where(targets >= 0, lse - picked, 0.0)
+
+
+def losses_shifted_target(logits, targets):
+    t = np.asarray(targets)
+    V = np.asarray(logits).shape[-1]
+    return _orig_token_losses(logits, np.where(t >= 0, (t + 1) % V, t))
+
+
+LOSS_MUTANTS = [
+    ("token_weights", weights_token_mean,
+     [lambda: lpins.test_packed_loss_equals_unpacked_training_with_padding(0)]),
+    ("token_weights", weights_ids_shared_across_rows, [lpins.test_same_id_in_two_rows_is_two_samples]),
+    ("token_losses", losses_without_max_shift, [lpins.test_uniform_logits_give_ln_v]),
+    ("token_losses", losses_shifted_target,
+     [lambda: lpins.test_packed_loss_equals_unpacked_training_with_padding(1)]),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(LOSS_MUTANTS)))
+def test_loss_pins_catch_mutant(idx, monkeypatch):
+    name, mutant, checks = LOSS_MUTANTS[idx]
+    monkeypatch.setattr(PL, name, mutant)
+    for check in checks:
+        with pytest.raises(AssertionError):
+            check()
+
+
 MUTANTS = [
     ("visibility", vis_strict_causal,
      [lambda: pins.test_brute_force_tiny(0), lambda: pins.test_matches_torch_sdpa_float64("single_causal")]),
