@@ -174,6 +174,31 @@ def decode_parts(lwm, li, torch, reps: int):
     return out
 
 
+def loss_part(lwm, li, torch, reps: int):
+    """Packed-loss reweighting over the packed 128K workload's samples with a 40192-entry
+    vocabulary: reads the bf16 logits once and writes their gradient once (HBM bound)."""
+    import numpy as np
+
+    w = li.WORKLOADS[WORKLOAD]
+    V = 40192
+    segs = li.workload_segments(w)
+    seg = torch.from_numpy(li.segment_ids_from_lengths([n for _, n in segs])[None].astype(np.int32)).cuda()
+    rng = np.random.default_rng(w.seed + 11)
+    tg = torch.from_numpy(rng.integers(0, V, (1, w.Sq)).astype(np.int32)).cuda()
+    x = li.device_normal((1, w.Sq, V), w.seed, 2.0, 5, torch.bfloat16, "cuda")
+    dl = torch.empty_like(x)
+    ws = torch.empty(lwm.lwm_attn_packed_loss_workspace_bytes(1, w.Sq, V, len(segs)), dtype=torch.uint8,
+                     device="cuda")
+    loss = torch.empty(4, dtype=torch.float32, device="cuda")
+    ms = time_events(lambda: lwm.lwm_attn_packed_loss(x, tg, seg, len(segs), loss, None, dl, ws), reps)
+    algo = 2 * x.numel() * 2 + w.Sq * 4 * 3
+    gbs = algo / (ms * 1e-3) / 1e9
+    print(f"[bench] packed loss 128K x {V}: {ms:.3f} ms, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+    del x, dl
+    return {"packed_loss_128k": {"ms": ms, "algo_bytes": algo, "gbs": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS,
+                                 "tokens": w.Sq, "vocab": V, "samples": len(segs)}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -307,6 +332,7 @@ def main() -> int:
     if not args.no_parts and not args.no_decode:
         del x, o, lse, dq, dk, dv, ws, table
         parts.update(decode_parts(lwm, li, torch, args.part_reps))
+        parts.update(loss_part(lwm, li, torch, args.part_reps))
 
     fwd_tflops = parts["fwd"]["tflops"] if parts else None
     bwd_ms = sum(parts[k]["ms"] for k in ("bwd_delta", "bwd_dq", "bwd_dkv")) if parts else None

@@ -201,6 +201,40 @@ int lwm_attn_bwd_phase(const lwm_attn_desc* desc, int32_t phase, const void* q, 
 int lwm_attn_rope(int32_t B, int32_t H, int32_t S, int32_t D, int32_t dtype, int64_t pos_offset,
                   double theta, int32_t inverse, const void* x, void* out, void* stream);
 
+/*
+ * Packed-sequence loss reweighting, the step after attention in the packed path: the LWM
+ * pages reweight the loss of a packed sequence so that it equals training its samples
+ * unpacked with padding, so that samples with many tokens (long videos) do not outweigh
+ * samples with few loss tokens (short answers) (deep dive, section "Masked sequence
+ * packing", second step of the recipe; abstract page, contribution (b)).  The pages give no
+ * formula; the reading: unpacked training averages over each sample's loss tokens, then
+ * over samples.  So with n_s the loss tokens of sample s and N the samples (over the whole
+ * batch) that have any, a loss token t of sample s has weight w_t = 1 / (N n_s), and
+ *   l_t = logsumexp(x_t) - x_t[y_t],    loss = sum_t w_t l_t,
+ *   dlogits_t = grad_scale * w_t * (softmax(x_t) - onehot(y_t)).
+ *   logits   [B,T,V] (dtype LWM_BF16 or LWM_F32), the next-token logits of each position;
+ *   targets  int32 [B,T]: the target token, or negative for a position with no loss;
+ *   seg      int32 [B,T]: the sample (segment id) of each position within its batch row, the
+ *            same ids the attention mask uses; negative for padding.  Ids must be below
+ *            num_segments; a sample is (batch row, id), ids need not be contiguous runs.
+ *            A loss token has seg in [0, num_segments) and target in [0, V); positions whose
+ *            target is outside [0, V) count as positions with no loss.
+ *   loss     float32 device scalar (written); 0 when there is no loss token.
+ *   token_loss float32 [B,T] or NULL: l_t for every position with a target in [0, V)
+ *            (also padding ones, which have weight 0), 0 elsewhere.
+ *   dlogits  [B,T,V] in the logits' dtype or NULL (loss only); rows with weight 0 are zero.
+ *   workspace  at least lwm_attn_packed_loss_workspace_bytes(B, T, V, num_segments) bytes;
+ *            contents on entry irrelevant.
+ * The loss is summed in a fixed order: repeated calls give identical bits.  Requires V a
+ * multiple of 8 in [8, 131072] (float32 logits: V <= 65536, else LWM_ERR_UNSUPPORTED),
+ * num_segments >= 1, B*T < 2^31; grad_scale finite.
+ */
+size_t lwm_attn_packed_loss_workspace_bytes(int32_t B, int32_t T, int32_t V, int32_t num_segments);
+int lwm_attn_packed_loss(int32_t B, int32_t T, int32_t V, int32_t num_segments, int32_t dtype,
+                         const void* logits, const int32_t* targets, const int32_t* seg,
+                         float grad_scale, float* loss, float* token_loss, void* dlogits,
+                         void* workspace, size_t ws_bytes, void* stream);
+
 /* Static, NUL-terminated name of a status code. */
 const char* lwm_attn_status_string(int status);
 

@@ -15,6 +15,8 @@ Convenience layers on top of those calls:
   rope                                    -- RoPE rotation of Q or K by global position
                                              (also the rope_theta option of the forward and
                                              backward layers)
+  packed_loss                             -- cross-entropy reweighted per packed sample,
+                                             with its gradient
 """
 from __future__ import annotations
 
@@ -41,6 +43,7 @@ EXPORTED = (
     "lwm_attn_merge_chunk", "lwm_attn_bwd_workspace_bytes", "lwm_attn_bwd",
     "lwm_attn_bwd_phase", "lwm_attn_status_string", "lwm_attn_version",
     "lwm_attn_decode_workspace_bytes", "lwm_attn_decode", "lwm_attn_rope",
+    "lwm_attn_packed_loss_workspace_bytes", "lwm_attn_packed_loss",
 )
 LWM_BWD_DELTA, LWM_BWD_DQ, LWM_BWD_DKV = 0, 1, 2
 
@@ -85,6 +88,9 @@ def load_library(path: str = LIB_PATH):
         "lwm_attn_decode_workspace_bytes": (SZ, [DP]),
         "lwm_attn_decode": (ctypes.c_int, [DP, P, P, P, P, P, P, P, P, P, SZ, P]),
         "lwm_attn_rope": (ctypes.c_int, [I32, I32, I32, I32, I32, I64, ctypes.c_double, I32, P, P, P]),
+        "lwm_attn_packed_loss_workspace_bytes": (SZ, [I32, I32, I32, I32]),
+        "lwm_attn_packed_loss": (ctypes.c_int, [I32, I32, I32, I32, I32, P, P, P, ctypes.c_float, P, P,
+                                                P, P, SZ, P]),
         "lwm_attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "lwm_attn_version": (ctypes.c_int, []),
     }
@@ -197,6 +203,39 @@ def lwm_attn_rope(x, out, pos_offset: int, theta: float, inverse: bool = False, 
     rc = load_library().lwm_attn_rope(B, H, S, D, _dtype_code(x.dtype), int(pos_offset), float(theta),
                                       int(bool(inverse)), _ptr(x), _ptr(out), _stream(stream))
     _check("lwm_attn_rope", rc)
+
+
+def lwm_attn_packed_loss_workspace_bytes(B: int, T: int, V: int, num_segments: int) -> int:
+    return int(load_library().lwm_attn_packed_loss_workspace_bytes(B, T, V, num_segments))
+
+
+def lwm_attn_packed_loss(logits, targets, seg, num_segments: int, loss, token_loss=None,
+                         dlogits=None, workspace=None, grad_scale: float = 1.0, stream=None):
+    """Reweighted packed cross-entropy of logits [B,T,V]; see include/lwm_attn.h."""
+    B, T, V = logits.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load_library().lwm_attn_packed_loss(B, T, V, int(num_segments), _dtype_code(logits.dtype),
+                                             _ptr(logits), _ptr(targets), _ptr(seg), float(grad_scale),
+                                             _ptr(loss), _ptr(token_loss), _ptr(dlogits),
+                                             _ptr(workspace), ws_bytes, _stream(stream))
+    _check("lwm_attn_packed_loss", rc)
+
+
+def packed_loss(logits, targets, seg, num_segments=None, *, grad=True, grad_scale=1.0, stream=None):
+    """(loss, token_loss, dlogits or None) with the packed-sample reweighting."""
+    import torch
+
+    B, T, V = logits.shape
+    if num_segments is None:
+        num_segments = int(seg.max().item()) + 1 if seg.numel() else 1
+    num_segments = max(1, num_segments)
+    ws = torch.empty(max(lwm_attn_packed_loss_workspace_bytes(B, T, V, num_segments), 16),
+                     dtype=torch.uint8, device=logits.device)
+    loss = torch.empty(4, dtype=torch.float32, device=logits.device)  # 16 bytes, aligned
+    tl = torch.empty((B, T), dtype=torch.float32, device=logits.device)
+    dl = torch.empty_like(logits) if grad else None
+    lwm_attn_packed_loss(logits, targets, seg, num_segments, loss, tl, dl, ws, grad_scale, stream)
+    return loss[0], tl, dl
 
 
 def lwm_attn_bwd_workspace_bytes(desc: Desc) -> int:

@@ -20,7 +20,8 @@ LIB = os.path.join(PKG, "liblwm_attn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "table.hip", "attn_f32.hip", "attn_bf16.hip", "merge.hip", "rope.hip"]
+SOURCES = ["api.cpp", "table.hip", "attn_f32.hip", "attn_bf16.hip", "merge.hip", "rope.hip",
+           "packed_loss.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result",

@@ -2,6 +2,7 @@
 // dtype and head width, launch on the caller's stream, error mapping.  Holds no state.
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <limits>
 
@@ -170,6 +171,43 @@ int lwm_attn_rope(int32_t B, int32_t H, int32_t S, int32_t D, int32_t dtype, int
   if (xa != oa && xa < oa + bytes && oa < xa + bytes) return LWM_ERR_INVALID_ARG;
   return hip_status(lwm::launch_rope(B, H, S, D, dtype, pos_offset, theta, inverse, x, out,
                                      static_cast<hipStream_t>(stream)));
+}
+
+static int check_packed_loss(int32_t B, int32_t T, int32_t V, int32_t nseg) {
+  if (B < 0 || T < 0 || nseg < 1) return LWM_ERR_SHAPE;
+  if (V < 8 || V % 8 != 0 || V > 131072) return LWM_ERR_UNSUPPORTED;
+  if (int64_t(B) * T >= (int64_t(1) << 31)) return LWM_ERR_SHAPE;  // one workgroup per token
+  if (int64_t(B) * nseg > (int64_t(1) << 31) / 4) return LWM_ERR_SHAPE;
+  if (int64_t(B) * T * V > (int64_t(1) << 42)) return LWM_ERR_SHAPE;
+  return LWM_OK;
+}
+
+size_t lwm_attn_packed_loss_workspace_bytes(int32_t B, int32_t T, int32_t V, int32_t num_segments) {
+  if (check_packed_loss(B, T, V, num_segments) != LWM_OK) return 0;
+  return lwm::packed_loss_layout(B, T, num_segments).total;
+}
+
+int lwm_attn_packed_loss(int32_t B, int32_t T, int32_t V, int32_t num_segments, int32_t dtype,
+                         const void* logits, const int32_t* targets, const int32_t* seg,
+                         float grad_scale, float* loss, float* token_loss, void* dlogits,
+                         void* workspace, size_t ws_bytes, void* stream) {
+  int rc = check_packed_loss(B, T, V, num_segments);
+  if (rc) return rc;
+  if (dtype != LWM_BF16 && dtype != LWM_F32) return LWM_ERR_INVALID_ARG;
+  if (dtype == LWM_F32 && V > 65536) return LWM_ERR_UNSUPPORTED;
+  if (!std::isfinite(grad_scale)) return LWM_ERR_INVALID_ARG;
+  if (!loss) return LWM_ERR_INVALID_ARG;
+  const bool any = int64_t(B) * T > 0;
+  if (any && (!logits || !targets || !seg)) return LWM_ERR_INVALID_ARG;
+  if (!workspace || ws_bytes < lwm_attn_packed_loss_workspace_bytes(B, T, V, num_segments))
+    return LWM_ERR_WORKSPACE;
+  const void* ptrs[] = {logits, targets, seg, loss, token_loss, dlogits, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return LWM_ERR_ALIGNMENT;
+  return hip_status(lwm::launch_packed_loss(lwm::packed_loss_layout(B, T, num_segments), B, T, V,
+                                            num_segments, dtype, logits, targets, seg, grad_scale,
+                                            loss, token_loss, dlogits, workspace,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 size_t lwm_attn_bwd_workspace_bytes(const lwm_attn_desc* d) {

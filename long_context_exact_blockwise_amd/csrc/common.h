@@ -91,6 +91,22 @@ inline DecodeLayout decode_layout(const lwm_attn_desc& d) {
   return L;
 }
 
+// Packed-loss workspace: per-sample loss-token counters int32 [B][nseg], the sample count
+// (one int32 in a 256-byte slot), then the weighted token losses float32 [B*T], each part on
+// a 256-byte boundary.
+struct PackedLossLayout {
+  size_t count_off, samples_off, wloss_off, total;
+};
+
+inline PackedLossLayout packed_loss_layout(int32_t B, int32_t T, int32_t nseg) {
+  PackedLossLayout L;
+  L.count_off = 0;
+  L.samples_off = align256(size_t(B) * nseg * sizeof(int32_t));
+  L.wloss_off = L.samples_off + 256;
+  L.total = L.wloss_off + align256(size_t(B) * T * sizeof(float));
+  return L;
+}
+
 // ---- launchers (each returns the launch status) ----------------------------------------
 
 // Zero `bytes` (a multiple of 16) at a 16-byte aligned device address.
@@ -127,6 +143,12 @@ hipError_t launch_bwd_bf16(const lwm_attn_desc& d, int phase, const void* q, con
 // RoPE over rows = B*H*S rows of D elements (D in 8..256, a power of two), in place allowed.
 hipError_t launch_rope(int32_t B, int32_t H, int32_t S, int32_t D, int32_t dtype, int64_t pos0,
                        double theta, int32_t inverse, const void* x, void* y, hipStream_t stream);
+
+hipError_t launch_packed_loss(const PackedLossLayout& L, int32_t B, int32_t T, int32_t V,
+                              int32_t nseg, int32_t dtype, const void* logits,
+                              const int32_t* targets, const int32_t* seg, float grad_scale,
+                              float* loss, float* token_loss, void* dlogits, void* workspace,
+                              hipStream_t stream);
 
 hipError_t launch_merge(int64_t rows, int32_t D, float* m, float* l, float* acc, const float* mc,
                         const float* lc, const float* accc, int32_t finalize, int32_t out_dtype,

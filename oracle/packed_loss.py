@@ -53,12 +53,10 @@ def token_losses(logits, targets):
     return np.where(targets >= 0, lse - picked, 0.0)
 
 
-def loss_and_grad(logits, targets, seg, grad_scale=1.0):
-    """(loss, per-token loss l [B,T], dlogits [B,T,V]) in float64."""
+def token_grads(logits, targets, w, grad_scale=1.0):
+    """dlogits [B,T,V] = grad_scale * w_t * (softmax(x_t) - onehot(y_t)) for given weights w
+    (rows may be any subset of positions, with their weights from the whole batch)."""
     x = np.asarray(logits, np.float64)
-    w = token_weights(targets, seg)
-    l = token_losses(x, targets)
-    loss = float(np.sum(w * l))
     m = x.max(axis=-1, keepdims=True)
     p = np.exp(x - m)
     p /= p.sum(axis=-1, keepdims=True)
@@ -66,5 +64,13 @@ def loss_and_grad(logits, targets, seg, grad_scale=1.0):
     onehot = np.zeros_like(p)
     b, t = np.nonzero(targets >= 0)
     onehot[b, t, targets[b, t]] = 1.0
-    grad = (grad_scale * w)[..., None] * (p - onehot)
-    return loss, l, grad
+    return (grad_scale * np.asarray(w, np.float64))[..., None] * (p - onehot)
+
+
+def loss_and_grad(logits, targets, seg, grad_scale=1.0):
+    """(loss, per-token loss l [B,T], dlogits [B,T,V]) in float64."""
+    x = np.asarray(logits, np.float64)
+    w = token_weights(targets, seg)
+    l = token_losses(x, targets)
+    loss = float(np.sum(w * l))
+    return loss, l, token_grads(x, targets, w, grad_scale)

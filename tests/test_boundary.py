@@ -220,3 +220,30 @@ def test_rope_rejects_bad_arguments(lib):
     assert call(out=FAKE + 8) == ALIGN
     assert call(out=FAKE + 256) == INVALID           # partial overlap with x
     assert call(S=0, x=None, out=None) == OK         # nothing to do
+
+
+def test_packed_loss_workspace_and_rejections(lib):
+    def al(x):
+        return (x + 255) // 256 * 256
+
+    assert lwm.lwm_attn_packed_loss_workspace_bytes(2, 1000, 40192, 30) == al(2 * 30 * 4) + 256 + al(2 * 1000 * 4)
+    assert lwm.lwm_attn_packed_loss_workspace_bytes(1, 10, 12, 1) == 0      # V % 8
+    assert lwm.lwm_attn_packed_loss_workspace_bytes(1, 10, 16, 0) == 0      # no segment
+    f = lib.lwm_attn_packed_loss
+
+    def call(B=1, T=100, V=40192, nseg=4, dtype=lwm.LWM_BF16, g=1.0, logits=FAKE, tg=FAKE, seg=FAKE,
+             loss=FAKE, tl=None, dl=FAKE, ws=FAKE, ws_bytes=1 << 30):
+        return f(B, T, V, nseg, dtype, logits, tg, seg, g, loss, tl, dl, ws, ws_bytes, None)
+
+    assert call(V=100) == UNSUP
+    assert call(V=262144) == UNSUP
+    assert call(V=131072, dtype=lwm.LWM_F32) == UNSUP
+    assert call(nseg=0) == SHAPE
+    assert call(T=-1) == SHAPE
+    assert call(dtype=5) == INVALID
+    assert call(g=float("nan")) == INVALID
+    assert call(loss=None) == INVALID
+    assert call(seg=None) == INVALID
+    assert call(ws=None) == WS
+    assert call(ws_bytes=100) == WS
+    assert call(dl=FAKE + 2) == ALIGN
