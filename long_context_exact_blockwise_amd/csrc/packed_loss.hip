@@ -12,9 +12,10 @@
 // Kernels, in stream order:
 //   count    one thread per token: integer atomic add into the per-sample counters;
 //   samples  one workgroup: N = number of counters above zero;
-//   ce       one workgroup of 1024 threads per token row: the row's logits are loaded once
-//            into registers (8 per chunk, R <= 16 chunks per thread for bf16, <= 8 for
-//            float32, hence V <= 131072 or 65536), max and sum of exponentials
+//   ce       one workgroup per token row, the smallest of 256, 512 or 1024 threads whose
+//            registers hold the row: the row's logits are loaded once into registers (8 per
+//            chunk, up to 24 chunks per thread for bf16 and 12 for float32; 1024 threads take
+//            V up to 131072 or 65536), max and sum of exponentials
 //            are reduced across the workgroup, then the gradient row is written; rows that
 //            are not loss tokens skip the load and write zeros;
 //   sum      one workgroup: the weighted token losses are summed in a fixed order, so the
@@ -29,8 +30,7 @@
 namespace lwm {
 namespace {
 
-constexpr int kCeThreads = 1024;
-constexpr int kWaves = kCeThreads / 64;
+constexpr int kMaxWaves = 16;  // largest workgroup: 1024 threads
 constexpr float kLog2e = 1.4426950408889634f;
 
 __global__ void __launch_bounds__(256) loss_count_kernel(int64_t tokens, int32_t T, int32_t V,
@@ -80,6 +80,7 @@ template <> struct Chunk<uint16_t> {
   }
   __device__ static void zero(uint16_t* p) { *reinterpret_cast<uint4*>(p) = make_uint4(0, 0, 0, 0); }
   __device__ static float at(const uint16_t* p) { return __uint_as_float(uint32_t(*p) << 16); }
+  __device__ static void put1(uint16_t* p, float v) { *reinterpret_cast<__bf16*>(p) = (__bf16)v; }
 };
 template <> struct Chunk<float> {
   float4 a, b;
@@ -100,7 +101,12 @@ template <> struct Chunk<float> {
     reinterpret_cast<float4*>(p)[1] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   __device__ static float at(const float* p) { return *p; }
+  __device__ static void put1(float* p, float v) { *p = v; }
 };
+
+// 2^x by the hardware instruction alone: results below 2^-126 flush to zero, which moves
+// neither a sum of exponentials nor a softmax probability stored in bf16 or float32.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -113,26 +119,26 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// Workgroup-wide reduction through LDS; every thread gets the result.
-template <bool kMax>
+// Workgroup-wide reduction through LDS over NW waves; every thread gets the result.
+template <bool kMax, int NW>
 __device__ __forceinline__ float block_reduce(float x, float* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   x = kMax ? wave_max(x) : wave_sum(x);
   if (lane == 0) red[wave] = x;
   __syncthreads();
-  float r = lane < kWaves ? red[lane] : (kMax ? -INFINITY : 0.f);
+  float r = lane < NW ? red[lane] : (kMax ? -INFINITY : 0.f);
   r = kMax ? wave_max(r) : wave_sum(r);
   __syncthreads();  // red is reused by the next reduction
   return r;
 }
 
-template <typename T, int R>
-__global__ void __launch_bounds__(kCeThreads)
+template <typename T, int NT, int R>
+__global__ void __launch_bounds__(NT)
 loss_ce_kernel(int32_t T_, int32_t V, int32_t nseg, float grad_scale, const T* __restrict__ X,
                const int32_t* __restrict__ tg, const int32_t* __restrict__ seg,
                const int32_t* __restrict__ cnt, const int32_t* __restrict__ nsamples,
                float* __restrict__ wloss, float* __restrict__ token_loss, T* __restrict__ dX) {
-  __shared__ float red[kWaves];
+  __shared__ float red[kMaxWaves];
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
   const int nch = V / 8;
@@ -146,7 +152,7 @@ loss_ce_kernel(int32_t T_, int32_t V, int32_t nseg, float grad_scale, const T* _
   T* dx = dX ? dX + row * V : nullptr;
   if (!target_ok) {  // not a loss token: no loss, zero gradient, the row is not read
     if (dx)
-      for (int c = tid; c < nch; c += kCeThreads) Chunk<T>::zero(dx + 8 * c);
+      for (int c = tid; c < nch; c += NT) Chunk<T>::zero(dx + 8 * c);
     if (tid == 0) {
       wloss[row] = 0.f;
       if (token_loss) token_loss[row] = 0.f;
@@ -156,32 +162,32 @@ loss_ce_kernel(int32_t T_, int32_t V, int32_t nseg, float grad_scale, const T* _
   Chunk<T> ch[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int c = tid + r * kCeThreads;
+    const int c = tid + r * NT;
     if (c < nch) ch[r].load(x + 8 * c);
   }
   float mx = -INFINITY;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    if (tid + r * kCeThreads < nch) {
+    if (tid + r * NT < nch) {
       float v[8];
       ch[r].get(v);
 #pragma unroll
       for (int e = 0; e < 8; ++e) mx = fmaxf(mx, v[e]);
     }
   }
-  mx = block_reduce<true>(mx, red);
+  mx = block_reduce<true, NT / 64>(mx, red);
   const float mx2 = mx * kLog2e;
   float sum = 0.f;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    if (tid + r * kCeThreads < nch) {
+    if (tid + r * NT < nch) {
       float v[8];
       ch[r].get(v);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sum += exp2f(fmaf(v[e], kLog2e, -mx2));
+      for (int e = 0; e < 8; ++e) sum += exp2_hw(fmaf(v[e], kLog2e, -mx2));
     }
   }
-  sum = block_reduce<false>(sum, red);
+  sum = block_reduce<false, NT / 64>(sum, red);
   const float lse = mx + logf(sum);
   if (tid == 0) {
     const float l = lse - Chunk<T>::at(x + y);
@@ -189,40 +195,78 @@ loss_ce_kernel(int32_t T_, int32_t V, int32_t nseg, float grad_scale, const T* _
     if (token_loss) token_loss[row] = l;
   }
   if (!dx) return;
-  // d/dx_j = g w (exp(x_j - lse) - [j == y]); exp(x_j - lse) = exp2(x_j log2e - lse log2e)
+  // d/dx_j = g w (exp(x_j - lse) - [j == y]); exp(x_j - lse) = exp2(x_j log2e - lse log2e).
+  // Every element is written as g w p_j first; the thread that wrote the target's chunk
+  // then rewrites the target element with g w (p_y - 1) (same thread, same address: the
+  // later store wins).
   const float gw = grad_scale * w;
   const float lse2 = lse * kLog2e;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int c = tid + r * kCeThreads;
+    const int c = tid + r * NT;
     if (c < nch) {
       float v[8];
       ch[r].get(v);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = exp2f(fmaf(v[e], kLog2e, -lse2));
-        v[e] = gw * (p - (8 * c + e == y ? 1.f : 0.f));
-      }
+      for (int e = 0; e < 8; ++e) v[e] = gw * exp2_hw(fmaf(v[e], kLog2e, -lse2));
       Chunk<T>::put(dx + 8 * c, v);
     }
+  }
+  if (tid == (y / 8) % NT) {
+    const float p = exp2_hw(fmaf(Chunk<T>::at(x + y), kLog2e, -lse2));
+    Chunk<T>::put1(dx + y, gw * (p - 1.f));
   }
 }
 
 __global__ void __launch_bounds__(1024) loss_sum_kernel(int64_t n, const float* __restrict__ wloss,
                                                         float* __restrict__ loss) {
-  __shared__ float red[kWaves];
+  __shared__ float red[kMaxWaves];
   float s = 0.f;
   for (int64_t i = threadIdx.x; i < n; i += 1024) s += wloss[i];
-  s = block_reduce<false>(s, red);
+  s = block_reduce<false, 16>(s, red);
   if (threadIdx.x == 0) loss[0] = s;
 }
 
-template <typename T, int R>
+template <typename T, int NT, int R>
 void ce(int64_t rows, int32_t T_, int32_t V, int32_t nseg, float g, const void* x, const int32_t* tg,
         const int32_t* seg, const int32_t* cnt, const int32_t* ns, float* wl, float* tl, void* dx,
         hipStream_t stream) {
-  loss_ce_kernel<T, R><<<dim3(unsigned(rows)), dim3(kCeThreads), 0, stream>>>(
+  loss_ce_kernel<T, NT, R><<<dim3(unsigned(rows)), dim3(NT), 0, stream>>>(
       T_, V, nseg, g, static_cast<const T*>(x), tg, seg, cnt, ns, wl, tl, static_cast<T*>(dx));
+}
+
+// Smallest workgroup whose registers hold the row: rows of up to 256 x 8 x 24 bf16 logits
+// (12 chunks for float32) fit a 256-thread workgroup, so several rows per CU are in flight.
+template <typename T>
+void ce_dispatch(int64_t rows, int32_t T_, int32_t V, int32_t nseg, float g, const void* x,
+                 const int32_t* tg, const int32_t* seg, const int32_t* cnt, const int32_t* ns,
+                 float* wl, float* tl, void* dx, hipStream_t stream) {
+  constexpr int kR = sizeof(T) == 2 ? 24 : 12;  // chunks a thread may hold
+  const int nch = V / 8;
+  const int per = (nch + 255) / 256;  // chunks per thread at 256 threads
+  if (per <= 4) {
+    ce<T, 256, 4>(rows, T_, V, nseg, g, x, tg, seg, cnt, ns, wl, tl, dx, stream);
+  } else if (per <= 8) {
+    ce<T, 256, 8>(rows, T_, V, nseg, g, x, tg, seg, cnt, ns, wl, tl, dx, stream);
+  } else if constexpr (sizeof(T) == 2) {  // bf16: tighter register tiles keep occupancy up
+    if (per <= 16)
+      ce<T, 256, 16>(rows, T_, V, nseg, g, x, tg, seg, cnt, ns, wl, tl, dx, stream);
+    else if (per <= 20)
+      ce<T, 256, 20>(rows, T_, V, nseg, g, x, tg, seg, cnt, ns, wl, tl, dx, stream);
+    else if (per <= kR)
+      ce<T, 256, kR>(rows, T_, V, nseg, g, x, tg, seg, cnt, ns, wl, tl, dx, stream);
+    else if ((nch + 511) / 512 <= kR)
+      ce<T, 512, kR>(rows, T_, V, nseg, g, x, tg, seg, cnt, ns, wl, tl, dx, stream);
+    else
+      ce<T, 1024, 16>(rows, T_, V, nseg, g, x, tg, seg, cnt, ns, wl, tl, dx, stream);
+    return;
+  } else if (per <= kR) {
+    ce<T, 256, kR>(rows, T_, V, nseg, g, x, tg, seg, cnt, ns, wl, tl, dx, stream);
+  } else if ((nch + 511) / 512 <= kR) {
+    ce<T, 512, kR>(rows, T_, V, nseg, g, x, tg, seg, cnt, ns, wl, tl, dx, stream);
+  } else {
+    ce<T, 1024, 8>(rows, T_, V, nseg, g, x, tg, seg, cnt, ns, wl, tl, dx, stream);
+  }
 }
 
 }  // namespace
@@ -243,17 +287,13 @@ hipError_t launch_packed_loss(const PackedLossLayout& L, int32_t B, int32_t T_, 
     loss_count_kernel<<<dim3(unsigned((tokens + 255) / 256)), dim3(256), 0, stream>>>(
         tokens, T_, V, nseg, targets, seg, cnt);
   loss_samples_kernel<<<dim3(1), dim3(256), 0, stream>>>(int64_t(B) * nseg, cnt, ns);
-  const int nch = V / 8;
-  const bool bf = dtype == LWM_BF16;
-  if (tokens == 0) {
-  } else if (nch <= 2 * kCeThreads) {
-    bf ? ce<uint16_t, 2>(tokens, T_, V, nseg, grad_scale, logits, targets, seg, cnt, ns, wl, token_loss, dlogits, stream)
-       : ce<float, 2>(tokens, T_, V, nseg, grad_scale, logits, targets, seg, cnt, ns, wl, token_loss, dlogits, stream);
-  } else if (nch <= 8 * kCeThreads) {
-    bf ? ce<uint16_t, 8>(tokens, T_, V, nseg, grad_scale, logits, targets, seg, cnt, ns, wl, token_loss, dlogits, stream)
-       : ce<float, 8>(tokens, T_, V, nseg, grad_scale, logits, targets, seg, cnt, ns, wl, token_loss, dlogits, stream);
-  } else {  // bf16 only: float32 rows this long would not fit the registers
-    ce<uint16_t, 16>(tokens, T_, V, nseg, grad_scale, logits, targets, seg, cnt, ns, wl, token_loss, dlogits, stream);
+  if (tokens > 0) {
+    if (dtype == LWM_BF16)
+      ce_dispatch<uint16_t>(tokens, T_, V, nseg, grad_scale, logits, targets, seg, cnt, ns, wl,
+                            token_loss, dlogits, stream);
+    else
+      ce_dispatch<float>(tokens, T_, V, nseg, grad_scale, logits, targets, seg, cnt, ns, wl,
+                         token_loss, dlogits, stream);
   }
   loss_sum_kernel<<<dim3(1), dim3(1024), 0, stream>>>(tokens, wl, loss);
   return hipGetLastError();

@@ -45,6 +45,13 @@ CASES = [
     ("max_vocab_bf16", 5, 1, 12, 131072, "bf16", 2, 0),
     ("max_vocab_f32", 6, 1, 12, 65536, "f32", 2, 0),
     ("ragged_vocab_bf16", 7, 2, 50, 1000, "bf16", 4, 5),
+    # one case per register tile the dispatch can pick (workgroup size x chunks per thread)
+    ("tile256x8_bf16", 8, 1, 20, 16384, "bf16", 3, 0),
+    ("tile256x16_llama_text_vocab_bf16", 9, 1, 20, 32000, "bf16", 3, 2),
+    ("tile256x24_bf16", 10, 1, 20, 49152, "bf16", 3, 0),
+    ("tile512x24_bf16", 11, 1, 16, 90000, "bf16", 3, 0),
+    ("tile256x8_f32", 12, 1, 20, 16000, "f32", 3, 0),
+    ("tile256x12_f32", 13, 1, 20, 24000, "f32", 3, 0),
 ]
 
 
