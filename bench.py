@@ -141,10 +141,11 @@ def blas_name() -> str:
     return "unknown"
 
 
-def decode_parts(lwm, li, torch, reps: int):
+def decode_parts(lwm, li, torch, reps: int, unsplit: bool = False):
     """Split-KV decode against a 1M-token cache (one and sixteen new rows per head): the
-    path streams K and V once, so it is priced against HBM bandwidth.  The unsplit forward
-    on the same inputs is timed once beside it."""
+    path streams K and V once, so it is priced against HBM bandwidth.  With `unsplit`, the
+    plain forward on the same inputs is timed once beside it (kept out of the default run so
+    that per-kernel profiles of the training forward see only its training launches)."""
     out = {}
     for name in ("decode_1m_q1", "decode_1m_q16"):
         w = li.WORKLOADS[name]
@@ -160,16 +161,18 @@ def decode_parts(lwm, li, torch, reps: int):
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device="cuda")
         ms = time_events(lambda: lwm.lwm_attn_decode(desc, q, k, v, sq, sk, table, o, lse, ws), reps)
-        ms_unsplit = time_events(lambda: lwm.lwm_attn_fwd(desc, lwm.LWM_OUT_FINAL, q, k, v, sq, sk,
-                                                          table, o=o, lse=lse), 1)
+        ms_unsplit = None
+        if unsplit:  # the training forward on the same inputs: one workgroup per (tile, head)
+            ms_unsplit = time_events(lambda: lwm.lwm_attn_fwd(desc, lwm.LWM_OUT_FINAL, q, k, v, sq, sk,
+                                                              table, o=o, lse=lse), 1)
         # algorithmic bytes: K and V once, Q and O once, LSE
         algo = 2 * w.B * w.H * w.Sk * w.D * 2 + 2 * w.B * w.H * w.Sq * w.D * 2 + 4 * w.B * w.H * w.Sq
         gbs = algo / (ms * 1e-3) / 1e9
         out[name] = {"ms": ms, "algo_bytes": algo, "gbs": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS,
                      "workspace_bytes": ws.numel(), "unsplit_fwd_ms": ms_unsplit,
                      "B": w.B, "H": w.H, "Sq": w.Sq, "Sk": w.Sk, "q_offset": w.q_offset}
-        print(f"[bench] {name}: {ms:.3f} ms, {gbs:.0f} GB/s (unsplit forward {ms_unsplit:.2f} ms)",
-              file=sys.stderr, flush=True)
+        print(f"[bench] {name}: {ms:.3f} ms, {gbs:.0f} GB/s"
+              + (f" (unsplit forward {ms_unsplit:.2f} ms)" if ms_unsplit else ""), file=sys.stderr, flush=True)
         del q, k, v, o, lse, ws, table
     return out
 
@@ -209,7 +212,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parts", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
-                    help="skip the split-KV decode parts (1M-token cache)")
+                    help="skip the decode and packed-loss parts")
+    ap.add_argument("--decode-unsplit", action="store_true",
+                    help="also time the plain forward on the decode inputs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy three times (HBM counter calibration)")
     args = ap.parse_args()
@@ -331,7 +336,7 @@ def main() -> int:
 
     if not args.no_parts and not args.no_decode:
         del x, o, lse, dq, dk, dv, ws, table
-        parts.update(decode_parts(lwm, li, torch, args.part_reps))
+        parts.update(decode_parts(lwm, li, torch, args.part_reps, args.decode_unsplit))
         parts.update(loss_part(lwm, li, torch, args.part_reps))
 
     fwd_tflops = parts["fwd"]["tflops"] if parts else None

@@ -33,14 +33,30 @@ namespace {
 constexpr int kMaxWaves = 16;  // largest workgroup: 1024 threads
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Packed samples are long runs of one id, so the lanes of a wave almost always count into
+// the same counter: the wave groups its lanes by counter (one round per distinct counter)
+// and one lane adds the group's size, instead of one atomic per token on a few addresses.
 __global__ void __launch_bounds__(256) loss_count_kernel(int64_t tokens, int32_t T, int32_t V,
                                                          int32_t nseg, const int32_t* __restrict__ tg,
                                                          const int32_t* __restrict__ seg,
                                                          int32_t* __restrict__ cnt) {
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= tokens) return;
-  const int32_t s = seg[i], y = tg[i];
-  if (s >= 0 && s < nseg && y >= 0 && y < V) atomicAdd(&cnt[(i / T) * nseg + s], 1);
+  int64_t key = -1;
+  if (i < tokens) {
+    const int32_t s = seg[i], y = tg[i];
+    if (s >= 0 && s < nseg && y >= 0 && y < V) key = (i / T) * nseg + s;
+  }
+  bool pending = key >= 0;
+  while (__ballot(pending) != 0) {
+    // the lowest pending lane's counter; every lane with the same counter joins its group
+    const uint64_t pend = __ballot(pending);
+    const int leader = __ffsll(static_cast<unsigned long long>(pend)) - 1;
+    const int64_t k = __shfl(key, leader);
+    const bool mine = pending && key == k;
+    const uint64_t group = __ballot(mine);
+    if (mine && int(threadIdx.x & 63) == leader) atomicAdd(&cnt[k], __popcll(group));
+    pending = pending && !mine;
+  }
 }
 
 __global__ void __launch_bounds__(256) loss_samples_kernel(int64_t n, const int32_t* __restrict__ cnt,
