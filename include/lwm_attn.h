@@ -168,7 +168,7 @@ int lwm_attn_bwd(const lwm_attn_desc* desc, const void* q, const void* k, const 
 
 /*
  * One phase of lwm_attn_bwd, same arguments and buffers.  The phases in order:
- *   LWM_BWD_DELTA  Delta = rowsum(dO * O) into the workspace;
+ *   LWM_BWD_DELTA  Delta = rowsum(dO * O) into the workspace (its own layout);
  *   LWM_BWD_DQ     dq from Delta (query-major pass over key tiles);
  *   LWM_BWD_DKV    dk, dv from Delta (key-major pass over query tiles).
  * DQ and DKV read the workspace DELTA wrote and are independent of each other, so a caller

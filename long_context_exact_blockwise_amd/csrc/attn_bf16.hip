@@ -335,7 +335,7 @@ __device__ __forceinline__ void fwd_bf16_body(AttnParams p, TableView t, int mod
     const float alpha = upd ? fast_exp2(m_run - mxc) : 1.f;
     if (upd) m_run = mxc;
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    float ps4[4] = {0.f, 0.f, 0.f, 0.f};
+    float ps4[4];  // four partial sums, each seeded with its first weight
     bf16x8 pb[4];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
@@ -345,7 +345,7 @@ __device__ __forceinline__ void fwd_bf16_body(AttnParams p, TableView t, int mod
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           pv[j] = fast_exp2(fmaf(sacc[sub][8 * a + j], c, -m_use));
-          ps4[j & 3] += pv[j];
+          ps4[j & 3] = (sub == 0 && a == 0 && j < 4) ? pv[j] : ps4[j & 3] + pv[j];
         }
         pb[2 * sub + a] = to_bf16x8(pv);
       }
@@ -515,7 +515,8 @@ __global__ void __launch_bounds__(NT) decode_combine_kernel(int64_t rows, int ns
 // backward
 // ---------------------------------------------------------------------------------------
 
-// Delta_i = <dO_i, O_i> and LSE_i * log2(e) (both float32), 16 lanes per row of 128.
+// -Delta_i = -<dO_i, O_i> (stored negated) and LSE_i * log2(e), both float32, 16 lanes per
+// row of 128.
 __global__ void __launch_bounds__(NT) delta_bf16_kernel(int64_t rows, const uint16_t* __restrict__ O,
                                                         const uint16_t* __restrict__ dO,
                                                         const float* __restrict__ LSE,
@@ -536,7 +537,7 @@ __global__ void __launch_bounds__(NT) delta_bf16_kernel(int64_t rows, const uint
 #pragma unroll
   for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 16);
   if (row < rows && part == 0) {
-    delta[row] = s;
+    delta[row] = -s;  // stored negated: the dP products start from it (see dq / dkv)
     // a row that sees no key (LSE = -inf) gets +inf, so exp2(s c - lse2) is 0 for every
     // key of it, masked or not, and never inf - inf
     const float l = LSE[row];
@@ -588,7 +589,7 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
     greg[s] = *reinterpret_cast<bf16x8*>(&g);
   }
   const float lse2 = qlive ? LSE2[r64] : 0.f;
-  const float dl = qlive ? delta[r64] : 0.f;
+  const float ndl = qlive ? delta[r64] : 0.f;  // -Delta of the lane's row
   const int32_t sq = qlive ? seg_q[int64_t(b) * p.Sq + qrow] : -1;
   const int dpos = clamp_dpos(p.q_offset, p.k_offset);
 
@@ -653,7 +654,7 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int i = 8 * a + j;
-          ds[j] = fast_exp2(fmaf(sacc[i], c, -lse2)) * (pacc[i] - dl);
+          ds[j] = fast_exp2(fmaf(sacc[i], c, -lse2)) * (pacc[i] + ndl);
         }
         dsb[2 * sub + a] = to_bf16x8(ds);
       }
@@ -714,7 +715,7 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
   uint16_t* const q_lds0 = qg_lds;
   uint16_t* const g_lds0 = qg_lds + kTileElems;
 
-  // per query row of the tile: LSE*log2(e), Delta and the segment id (as raw 32-bit words)
+  // per query row of the tile: LSE*log2(e), -Delta and the segment id (as raw 32-bit words)
   __shared__ __attribute__((aligned(16))) float row_lds[2 * 3 * TB];
   __shared__ uint8_t stat_lds[kStatChunk];
 
@@ -782,7 +783,16 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
 
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-      f32x16 sacc = f32x16{0}, pacc = f32x16{0};
+      // dP starts from -Delta of each query row (slot 8a + j holds row 32 sub + 16a + 8hf + j),
+      // so the products deliver dP - Delta directly
+      f32x16 sacc = f32x16{0}, pacc;
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        float ndl[8];
+        lds_load_f8(rb_lds + TB + 32 * sub + 16 * a + 8 * hf, ndl);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pacc[8 * a + j] = ndl[j];
+      }
       const int qrow = 32 * sub + kperm(col);
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
@@ -811,15 +821,14 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         const int qbase = 32 * sub + 16 * a + 8 * hf;  // 8 consecutive local query rows
-        float lsev[8], dlv[8];
+        float lsev[8];
         lds_load_f8(rb_lds + qbase, lsev);
-        lds_load_f8(rb_lds + TB + qbase, dlv);
         float pv[8], ds[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int i = 8 * a + j;
           pv[j] = fast_exp2(fmaf(sacc[i], c, -lsev[j]));
-          ds[j] = pv[j] * (pacc[i] - dlv[j]);
+          ds[j] = pv[j] * pacc[i];
         }
         pb[a] = to_bf16x8(pv);
         dsb[a] = to_bf16x8(ds);
@@ -913,7 +922,7 @@ hipError_t launch_decode_bf16(const lwm_attn_desc& d, const void* q, const void*
   return hipGetLastError();
 }
 
-// Workspace: Delta [rows] then LSE * log2(e) [rows], rows = B*H*Sq, each 256-byte aligned.
+// Workspace: -Delta [rows] then LSE * log2(e) [rows], rows = B*H*Sq, each 256-byte aligned.
 hipError_t launch_bwd_bf16(const lwm_attn_desc& d, int phase, const void* q, const void* k,
                            const void* v, const void* o, const void* dO, const float* lse,
                            const int32_t* seg_q, const int32_t* seg_k, const void* table,
