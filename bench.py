@@ -106,8 +106,11 @@ def cpu_baseline(x_dev, lengths, scale, D, budget_s: float):
         if time.perf_counter() - t0 >= budget_s:
             break
     elapsed = time.perf_counter() - t0
+    # the oracle forms the whole W x W masked score matrix; its dense rate counts every pair
+    dense_flops = 14 * D * W * W * heads_done
     return {
         "value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+        "dense_value": dense_flops / elapsed / 1e12,
         "sample": f"NumPy float64 oracle, full masked score matrix, forward+backward of a "
                   f"{W}-token window at segment start {s0} of the same 131072-token packed "
                   f"layout, {heads_done} head(s), {elapsed:.1f} s; unmasked FLOPs (14*D per "
@@ -333,6 +336,10 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x, lengths, w.scale, w.D, args.cpu_seconds)
+        # extrapolations (not measured): the whole step on the CPU at the measured rates
+        cpu["extrapolated_step_s_visible_pairs"] = flops_step / (cpu["value"] * 1e12)
+        cpu["extrapolated_step_s_dense_matrix"] = (14 * w.D * w.Sq * w.Sq * w.H * w.B
+                                                   / (cpu["dense_value"] * 1e12))
 
     if not args.no_parts and not args.no_decode:
         del x, o, lse, dq, dk, dv, ws, table
@@ -351,6 +358,8 @@ def main() -> int:
                    "flops_per_step": flops_step,
                    "flop_count": "14*D per visible (query,key) pair per head: fwd 4*D + bwd 10*D"},
         "frac_of_bf16_peak": value / PEAK_BF16_TFLOPS,
+        # the same step counted as 12*D per pair (backward without the recompute of Q K^T)
+        "value_12D_convention": value * 12 / 14,
         "fwd_tflops": fwd_tflops,
         "fwd_frac_of_peak": (fwd_tflops / PEAK_BF16_TFLOPS) if fwd_tflops else None,
         "bwd_tflops_10D": (10 * unit_flops / (bwd_ms * 1e-3) / 1e12) if bwd_ms else None,

@@ -55,3 +55,14 @@ def max_abs(a, b):
     both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
     d = np.where(both_inf, 0.0, np.abs(a - b))
     return float(np.max(d))
+
+
+def rel_errors(got, ref):
+    """(max-abs / max-|ref|, relative Frobenius error) of a gradient, both reported beside
+    the max-abs bar."""
+    g = np.asarray(got, np.float64)
+    r = np.asarray(ref, np.float64)
+    mref = float(np.max(np.abs(r))) if r.size else 0.0
+    nref = float(np.linalg.norm(r))
+    mabs = float(np.max(np.abs(g - r))) if r.size else 0.0
+    return (mabs / mref if mref > 0 else 0.0), (float(np.linalg.norm(g - r)) / nref if nref > 0 else 0.0)

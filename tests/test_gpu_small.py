@@ -9,7 +9,8 @@ import pytest
 import lwm_inputs as li
 from oracle import attention as A
 import test_oracle_pins as pins
-from gpu_helpers import TOL_GRAD, TOL_LSE, TOL_O, f64, host_f64, max_abs, say, seg_dev, to_dev
+from gpu_helpers import (TOL_GRAD, TOL_LSE, TOL_O, f64, host_f64, max_abs, rel_errors, say,
+                         seg_dev, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -77,6 +78,9 @@ def test_bf16_forward_and_backward(case):
     eo, el = max_abs(f64(o), o_ref), max_abs(f64(lse), lse_ref)
     eq, ek, ev = max_abs(f64(dq), dq_ref), max_abs(f64(dk), dk_ref), max_abs(f64(dv), dv_ref)
     say(f"  max-abs O {eo:.2e} LSE {el:.2e} dQ {eq:.2e} dK {ek:.2e} dV {ev:.2e}")
+    rel = [rel_errors(f64(g), r) for g, r in ((dq, dq_ref), (dk, dk_ref), (dv, dv_ref))]
+    say("  gradients max-abs/max-ref, relative Frobenius: "
+        + ", ".join(f"{n} {a:.1e} {b:.1e}" for n, (a, b) in zip(("dQ", "dK", "dV"), rel)))
     assert np.array_equal(np.isinf(f64(lse)), np.isinf(lse_ref))
     assert eo <= TOL_O["bf16"] and el <= TOL_LSE
     assert eq <= TOL_GRAD["bf16"] and ek <= TOL_GRAD["bf16"] and ev <= TOL_GRAD["bf16"]
