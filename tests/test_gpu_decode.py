@@ -156,3 +156,30 @@ def test_decode_1m_cache(wname):
         del vh
     say(f"  Q = 0: max-abs LSE {e_lse:.2e} (all rows, all heads), O {e_o:.2e} (2 heads)")
     assert e_lse <= TOL_LSE and e_o <= TOL_O["bf16"]
+
+
+def test_plain_forward_on_1m_cache_walks_status_chunks():
+    """The plain forward on the 16-row decode inputs: one query tile sees 16384 key tiles,
+    staged in LDS 2048 at a time.  Against the decode result and, on two heads, the oracle."""
+    w = li.WORKLOADS["decode_1m_q16"]
+    say(f"{w.name}: plain forward over 16384 key tiles vs decode and the oracle")
+    desc, q, k, v, sq, sk, seg_q, seg_k = decode_full(w)
+    o_d, lse_d, table = decode(desc, q, k, v, sq, sk)
+    o_f = torch.empty_like(q)
+    lse_f = torch.empty_like(lse_d)
+    lwm.lwm_attn_fwd(desc, lwm.LWM_OUT_FINAL, q, k, v, sq, sk, table, o=o_f, lse=lse_f)
+    torch.cuda.synchronize()
+    fo, fl = max_abs(f64(o_f), f64(o_d)), max_abs(f64(lse_f), f64(lse_d))
+    rows = np.arange(w.Sq)
+    worst = [0.0, 0.0]
+    for h in (0, w.H - 1):
+        qh = q[0, h].float().cpu().numpy().astype(np.float64)
+        kh = k[0, h].float().cpu().numpy().astype(np.float64)
+        vh = v[0, h].float().cpu().numpy().astype(np.float64)
+        o_ref, lse_ref = A.forward_rows(qh, kh, vh, seg_q[0], seg_k[0], w.q_offset + rows, w.scale)
+        worst[0] = max(worst[0], max_abs(f64(o_f[0, h]), o_ref))
+        worst[1] = max(worst[1], max_abs(f64(lse_f[0, h]), lse_ref))
+        del kh, vh
+    say(f"  forward vs decode: O {fo:.2e} LSE {fl:.2e}; vs oracle: O {worst[0]:.2e} LSE {worst[1]:.2e}")
+    assert fo <= TOL_O["bf16"] and fl <= TOL_LSE
+    assert worst[0] <= TOL_O["bf16"] and worst[1] <= TOL_LSE

@@ -257,3 +257,48 @@ def test_packed_128k_closed_forms_all_rows():
     assert err_lse <= TOL_LSE
     assert err_dk == 0.0
     assert err_dv <= TOL_GRAD["bf16"]
+
+
+def test_long_single_segment_status_chunks():
+    """A single causal segment of 147456 tokens (2304 tiles of 64, more than the 2048 tile
+    classes a workgroup stages in LDS at a time), so the forward/dQ (last query tiles) and
+    dK/dV (first key tiles) walk their tile range in two chunks.  Sampled rows of O, LSE and
+    dQ against the oracle; Q = 0 closed forms on every row and key: LSE = ln(i + 1),
+    dK = 0, dV by suffix sums."""
+    S, H, D, seed = 147456, 2, 128, 41
+    scale = 1 / math.sqrt(D)
+    say(f"single segment S={S} H={H}: status staged in two chunks; sampled rows + Q = 0 closed forms")
+    seg = torch.zeros((1, S), dtype=torch.int32, device="cuda")
+    q, k, v, do = (li.device_normal((1, H, S, D), seed, 0.1 if i == 3 else 0.5, i, torch.bfloat16, "cuda")
+                   for i in range(4))
+    o, lse, table = lwm.attention_forward(q, k, v, seg, seg)
+    dq, dk, dv = lwm.attention_backward(q, k, v, o, do, lse, seg, seg, table)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 63, 64, 131071, 131072, 140000, S - 65, S - 1],
+                                     np.random.default_rng(seed).integers(0, S, 24)]))
+    seg_np = np.zeros(S, np.int32)
+    worst = [0.0, 0.0, 0.0]
+    for h in range(H):
+        qh, kh, vh, dh = (head_f64(t, 0, h) for t in (q, k, v, do))
+        o_ref, lse_ref = A.forward_rows(qh[rows], kh, vh, seg_np[rows], seg_np, rows, scale)
+        dq_ref = A.dq_rows(qh[rows], kh, vh, dh[rows], seg_np[rows], seg_np, rows, scale)
+        worst[0] = max(worst[0], max_abs(f64(o[0, h])[rows], o_ref))
+        worst[1] = max(worst[1], max_abs(f64(lse[0, h])[rows], lse_ref))
+        worst[2] = max(worst[2], max_abs(f64(dq[0, h])[rows], dq_ref))
+    say(f"  sampled rows: O {worst[0]:.2e} LSE {worst[1]:.2e} dQ {worst[2]:.2e}")
+    assert worst[0] <= TOL_O["bf16"] and worst[1] <= TOL_LSE and worst[2] <= TOL_GRAD["bf16"]
+    del o, lse, dq, dk, dv
+    q0 = torch.zeros_like(q)
+    o, lse, table = lwm.attention_forward(q0, k, v, seg, seg, table=table)
+    dq, dk, dv = lwm.attention_backward(q0, k, v, o, do, lse, seg, seg, table)
+    torch.cuda.synchronize()
+    cnt = np.arange(1, S + 1, dtype=np.float64)
+    err_lse = max_abs(f64(lse)[0], np.log(cnt)[None].repeat(H, 0))
+    err_dk = float(dk.float().abs().max())
+    err_dv = 0.0
+    for h in range(H):
+        dh = head_f64(do, 0, h)
+        ref = np.cumsum((dh / cnt[:, None])[::-1], axis=0)[::-1]
+        err_dv = max(err_dv, max_abs(f64(dv[0, h]), ref))
+    say(f"  Q = 0: LSE {err_lse:.2e} |dK| {err_dk:.2e} dV {err_dv:.2e}")
+    assert err_lse <= TOL_LSE and err_dk == 0.0 and err_dv <= TOL_GRAD["bf16"]
