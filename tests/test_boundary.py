@@ -247,3 +247,20 @@ def test_packed_loss_workspace_and_rejections(lib):
     assert call(ws=None) == WS
     assert call(ws_bytes=100) == WS
     assert call(dl=FAKE + 2) == ALIGN
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/lwm_attn.h is a C header: it compiles as C99 with warnings as errors."""
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "use_header.c"
+    src.write_text('#include "lwm_attn.h"\n'
+                   "int main(void) { lwm_attn_desc d = {0}; (void)d;\n"
+                   "  return lwm_attn_version() > 0 ? 0 : 1; }\n")
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
+                        "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
