@@ -284,3 +284,43 @@ def test_q_zero_closed_form_all_rows():
         cnt[s:e] = n
     assert max_abs(f64(o)[0], ref) <= TOL_O["bf16"]
     assert max_abs(f64(lse)[0], np.log(cnt)[None].repeat(H, 0)) <= TOL_LSE
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_batch_rows_with_different_layouts(dt):
+    """Each batch row has its own packing (segment cuts, padding, one row a single segment), so
+    segment ids, the block table and the kernels must index the batch row correctly; forward,
+    backward and decode against the oracle on every element."""
+    B, H, Sq, Sk, q_off, k_off = 3, 2, 450, 520, 70, 0
+    D = 128 if dt == "bf16" else 64
+    say(f"batch rows with different layouts ({dt}): B={B} Sq={Sq} Sk={Sk} q_off={q_off}")
+    rng = np.random.default_rng(77)
+    total = max(q_off + Sq, k_off + Sk)
+    layouts = [pins.random_layout(rng, total, allow_padding=False),
+               pins.random_layout(rng, total, allow_padding=True),
+               np.zeros(total, np.int32)]
+    seg_q = np.stack([l[q_off:q_off + Sq] for l in layouts]).astype(np.int32)
+    seg_k = np.stack([l[k_off:k_off + Sk] for l in layouts]).astype(np.int32)
+    x, _, _ = make_case(78, B, H, Sq, Sk, D, dt, "single", q_off, k_off)
+    scale = 1 / math.sqrt(D)
+    o_ref, lse_ref, (dq_ref, dk_ref, dv_ref) = run_oracle(x, seg_q, seg_k, dt, scale, True, q_off, k_off)
+    q, k, v, do = (to_dev(x[n], dt) for n in ("q", "k", "v", "do"))
+    sq, sk = seg_dev(seg_q), seg_dev(seg_k)
+    o, lse, table = lwm.attention_forward(q, k, v, sq, sk, q_offset=q_off, k_offset=k_off)
+    dq, dk, dv = lwm.attention_backward(q, k, v, o, do, lse, sq, sk, table, q_offset=q_off,
+                                        k_offset=k_off)
+    torch.cuda.synchronize()
+    errs = [max_abs(f64(o), o_ref), max_abs(f64(lse), lse_ref), max_abs(f64(dq), dq_ref),
+            max_abs(f64(dk), dk_ref), max_abs(f64(dv), dv_ref)]
+    if dt == "bf16":
+        od, lsed, _ = lwm.attention_decode(q, k, v, sq, sk, q_offset=q_off, k_offset=k_off, table=table)
+        torch.cuda.synchronize()
+        errs += [max_abs(f64(od), o_ref), max_abs(f64(lsed), lse_ref)]
+    say("  max-abs O {:.2e} LSE {:.2e} dQ {:.2e} dK {:.2e} dV {:.2e}".format(*errs[:5])
+        + (" decode O {:.2e} LSE {:.2e}".format(*errs[5:]) if dt == "bf16" else ""))
+    assert np.array_equal(np.isinf(f64(lse)), np.isinf(lse_ref))
+    tol_lse = TOL_LSE if dt == "bf16" else 1e-5
+    assert errs[0] <= TOL_O[dt] and errs[1] <= tol_lse
+    assert max(errs[2:5]) <= TOL_GRAD[dt]
+    if dt == "bf16":
+        assert errs[5] <= TOL_O[dt] and errs[6] <= TOL_LSE
