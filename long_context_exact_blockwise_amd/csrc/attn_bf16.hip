@@ -658,13 +658,29 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
         }
         dsb[2 * sub + a] = to_bf16x8(ds);
       }
-      // keep the two 32-key halves apart: overlapping them would need a second set of
-      // score registers, which does not fit beside two waves per SIMD
+      if (sub == 1) {
+        // dQ of the first 32 keys needs only their dS, so its MFMAs run under the second
+        // half's softmax: one MFMA per two operand reads and eight VALU instructions
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+            dqacc[db] = mfma32(lds_load_tr8(kb_lds, 16 * ks, 32 * db, lane), dsb[ks], dqacc[db]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 6);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 6);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 6);
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 6);
+        }
+      }
+      // keep the two 32-key halves' scores apart: overlapping them would need a second set
+      // of score registers, which does not fit beside two waves per SIMD
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks)
+    for (int ks = 2; ks < BK / 16; ++ks)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
         dqacc[db] = mfma32(lds_load_tr8(kb_lds, 16 * ks, 32 * db, lane), dsb[ks], dqacc[db]);
