@@ -15,11 +15,12 @@
 //
 // Streaming: tiles are double-buffered in LDS and filled by the buffer unit directly
 // (buffer_load ... lds), so no registers hold tile data in flight; the loads for tile j+1
-// are issued right after the barrier that opens tile j, and one barrier per tile both
-// publishes tile j+1 and retires the buffer tile j-1 used.  The loop body is instantiated
-// once per buffer half so every LDS address is a register plus a constant offset.  Each tile is stored once,
-// row-major and swizzled (mfma_tile.h); operands that run across its rows (V^T, K^T, Q^T,
-// dO^T) are read with the gfx950 transposing LDS read.
+// go out one instruction at a time between the first score MFMAs of tile j, after the
+// barrier that opens it, and one barrier per tile both publishes tile j+1 and retires the
+// buffer tile j-1 used.  The loop body is instantiated once per buffer half so every LDS
+// address is a register plus a constant offset.  Each tile is stored once, row-major and
+// swizzled (mfma_tile.h); operands that run across its rows (V^T, K^T, Q^T, dO^T) are read
+// with the gfx950 transposing LDS read.
 
 #include <climits>
 #include <cmath>
@@ -173,17 +174,22 @@ __device__ __forceinline__ void dma4(const i32x4& rsrc, uint32_t lds_base, uint3
 // into a swizzled LDS tile.  Each wave moves 4 blocks of 4 rows (1 KiB each); the buffer
 // unit writes lane l's 16 bytes to block + 16 l, so lane l fetches the logical chunk that
 // belongs at physical chunk l % 16 of its row.  Rows past nrows arrive as zeros.
+// Instruction `it` of wave w covers rows 16 it + 4 w + lane / 16.  The swizzle depends on the
+// row modulo 16 only, so the four instructions share one lane offset and differ in the
+// buffer base (a 16-row step), which keeps the per-lane state to one register; `wave` must
+// be wave-uniform so that the LDS bases stay scalar.
+__device__ __forceinline__ uint32_t tile_lane_off(int wave, int lane) {
+  const int row = 4 * wave + (lane >> 4);
+  return row * (D * 2) + (((lane & 15) ^ tile_swz(row)) << 4);
+}
 __device__ __forceinline__ void tile_async_load(uint16_t* tile, const uint16_t* __restrict__ src,
                                                 int row0, int nrows, int wave, int lane) {
-  const i32x4 rs = make_rsrc(src + int64_t(row0) * D, min(nrows - row0, BK) * D * 2);
-  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(tile));
+  const uint32_t voff = tile_lane_off(wave, lane);
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(tile)) + wave * 1024;
+  const int nb = min(nrows - row0, BK) * D * 2;
 #pragma unroll
-  for (int it = 0; it < BK / 16; ++it) {
-    const int blk = it * 4 + wave;
-    const int row = 4 * blk + (lane >> 4);
-    const uint32_t voff = row * (D * 2) + (((lane & 15) ^ tile_swz(row)) << 4);
-    dma16(rs, __builtin_amdgcn_readfirstlane(base + blk * 1024), voff);
-  }
+  for (int it = 0; it < BK / 16; ++it)
+    dma16(make_rsrc(src + int64_t(row0 + 16 * it) * D, nb - it * 16 * D * 2), base + it * 4096, voff);
 }
 
 // Issue the load of 64 consecutive 32-bit values (rows row0.. of a per-row vector) into LDS;
@@ -192,6 +198,68 @@ __device__ __forceinline__ void vec_async_load(void* dst, const void* src, int r
                                                int lane) {
   const i32x4 rs = make_rsrc(static_cast<const char*>(src) + int64_t(row0) * 4, min(nrows - row0, BK) * 4);
   dma4(rs, __builtin_amdgcn_readfirstlane(lds_addr(dst)), lane * 4);
+}
+
+// The same loads for a pair of tiles (K and V, or Q and dO), one instruction per call:
+// 0-3 fill the first tile, 4-7 the second.  Issued all at once after the barrier, the eight
+// instructions of each of the four waves queue behind the buffer unit, which moves one
+// 1 KiB instruction every 16 cycles or so, and the waves stall for hundreds of cycles
+// before their first MFMA; issued one at a time between the score MFMAs, they drain
+// while the matrix pipe works.
+struct PairDma {
+  const uint16_t* a;
+  const uint16_t* b;
+  int nb;
+  uint32_t ba, bb, voff;
+  __device__ __forceinline__ PairDma(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+                                     int row0, int nrows, uint16_t* da, uint16_t* db, int wave,
+                                     int lane)
+      : a(A + int64_t(row0) * D), b(B + int64_t(row0) * D), nb(min(nrows - row0, BK) * D * 2),
+        ba(__builtin_amdgcn_readfirstlane(lds_addr(da)) + wave * 1024),
+        bb(__builtin_amdgcn_readfirstlane(lds_addr(db)) + wave * 1024),
+        voff(tile_lane_off(wave, lane)) {}
+  __device__ __forceinline__ void operator()(int i) const {
+    const int it = i & 3;
+    dma16(make_rsrc((i < 4 ? a : b) + it * 16 * D, nb - it * 16 * D * 2), (i < 4 ? ba : bb) + it * 4096,
+          voff);
+  }
+};
+struct NoDma {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
+// Operand reads after which a chain of 16 MFMAs (reads running four ahead) issues one of the
+// eight tile loads: reads 4, 5, 7, 8, 10, 11, 13 and 14, about one load per 1.5 MFMAs.
+constexpr unsigned kDmaSlots = 0x6db0;
+template <class Dma>
+__device__ __forceinline__ void dma_after_read(const Dma& dma, int j) {
+  if ((kDmaSlots >> j) & 1) dma(__builtin_popcount(kDmaSlots & ((1u << j) - 1)));
+}
+
+// dQ / dK-dV score chains with the next tile's loads spread between them: S = A_tile . ra
+// and dP = B_tile . rb over D (16 MFMAs, the A and B operand reads alternating four ahead).
+template <class Dma>
+__device__ __forceinline__ void sdp_chain(f32x16& sacc, f32x16& pacc, const uint16_t* ab,
+                                          const uint16_t* bb, int row, int hf, const bf16x8* ra,
+                                          const bf16x8* rb, const Dma& dma) {
+  bf16x8 op[2 * D / 16];
+#pragma unroll
+  for (int j = 0; j < 2 * D / 16; ++j) {
+    op[j] = lds_load8(((j & 1) ? bb : ab) + tile_off(row, 16 * (j >> 1) + 8 * hf));
+    dma_after_read(dma, j);
+  }
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    sacc = mfma32(op[2 * s], ra[s], sacc);
+    pacc = mfma32(op[2 * s + 1], rb[s], pacc);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 3);
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 3);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 3);
 }
 
 // Wait until this wave's outstanding vector-memory loads (including loads into LDS) are done.
@@ -228,7 +296,8 @@ __device__ __forceinline__ void fwd_bf16_body(AttnParams p, TableView t, int mod
   const int qt = nqt - 1 - rest % nqt;
   const int b = rest / nqt;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, col = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t bh = int64_t(b) * p.H + h;
   const uint16_t* Qh = Q + bh * p.Sq * D;
   const uint16_t* Kh = K + bh * p.Sk * D;
@@ -273,31 +342,21 @@ __device__ __forceinline__ void fwd_bf16_body(AttnParams p, TableView t, int mod
     if (wave == 0) vec_async_load(sd, segk_b, kt * BK, p.Sk, lane);
   };
 
-  // One key tile: wait for its loads, start the next tile's loads into the other buffers,
-  // then S^T, mask, online softmax and O^T += V^T P^T.
-  int kt = 0, c0 = 0, c1 = -1;
-  auto step = [&](const uint16_t* kb_lds, const uint16_t* vb_lds, const int32_t* sb_lds,
-                  uint16_t* kn_lds, uint16_t* vn_lds, int32_t* sn_lds) {
-    const int st = uniform(stat_lds[kt - c0]);
-    const int kn = next_live_lds(stat_lds, c0, kt + 1, c1);
-    wait_vmem();
-    __syncthreads();
-    if (kn <= c1) issue(kn, kn_lds, vn_lds, sn_lds);
-    if (!wave_live) {
-      kt = kn;
-      return;
+  // S^T = K Q^T for two 32-key blocks (K rows loaded in kperm order).  The operand reads run
+  // four MFMAs ahead so LDS latency hides behind the matrix pipe; the next tile's loads
+  // (`dma`) go out between them.
+  auto scores = [&](f32x16* sacc, const uint16_t* kb_lds, const auto& dma) {
+    bf16x8 kop[2 * D / 16];
+#pragma unroll
+    for (int j = 0; j < 2 * D / 16; ++j) {
+      kop[j] = lds_load8(kb_lds + tile_off(32 * (j / (D / 16)) + kperm(col), 16 * (j % (D / 16)) + 8 * hf));
+      dma_after_read(dma, j);
     }
-
-    // S^T = K Q^T for two 32-key blocks (K rows loaded in kperm order).  The operand reads
-    // run four MFMAs ahead so LDS latency hides behind the matrix pipe.
-    f32x16 sacc[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       sacc[sub] = f32x16{0};
-      const int krow = 32 * sub + kperm(col);
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s)
-        sacc[sub] = mfma32(lds_load8(kb_lds + tile_off(krow, 16 * s + 8 * hf)), qreg[s], sacc[sub]);
+      for (int s = 0; s < D / 16; ++s) sacc[sub] = mfma32(kop[sub * (D / 16) + s], qreg[s], sacc[sub]);
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
 #pragma unroll
@@ -306,6 +365,31 @@ __device__ __forceinline__ void fwd_bf16_body(AttnParams p, TableView t, int mod
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+  };
+
+  // One key tile: wait for its loads, then S^T (starting the next tile's loads into the
+  // other buffers), mask, online softmax and O^T += V^T P^T.
+  int kt = 0, c0 = 0, c1 = -1;
+  auto step = [&](const uint16_t* kb_lds, const uint16_t* vb_lds, const int32_t* sb_lds,
+                  uint16_t* kn_lds, uint16_t* vn_lds, int32_t* sn_lds) {
+    const int st = uniform(stat_lds[kt - c0]);
+    const int kn = next_live_lds(stat_lds, c0, kt + 1, c1);
+    wait_vmem();
+    __syncthreads();
+    const bool more = kn <= c1;
+    if (!wave_live) {
+      if (more) issue(kn, kn_lds, vn_lds, sn_lds);
+      kt = kn;
+      return;
+    }
+
+    f32x16 sacc[2];
+    if (more) {
+      scores(sacc, kb_lds, PairDma(Kh, Vh, kn * BK, p.Sk, kn_lds, vn_lds, wave, lane));
+      if (wave == 0) vec_async_load(sn_lds, segk_b, kn * BK, p.Sk, lane);
+    } else {
+      scores(sacc, kb_lds, NoDma{});
+    }
 
     if (st == LWM_TILE_PARTIAL) {
       // branch-free visibility; rows past Sq carry sq = -1 and see nothing
@@ -568,7 +652,8 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
   const int rest = idx / p.H;
   const int qt = nqt - 1 - rest % nqt;
   const int b = rest / nqt;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, col = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t bh = int64_t(b) * p.H + h;
   const uint16_t* Kh = K + bh * p.Sk * D;
   const uint16_t* Vh = V + bh * p.Sk * D;
@@ -619,7 +704,8 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
     const int kn = next_live_lds(stat_lds, c0, kt + 1, c1);
     wait_vmem();
     __syncthreads();
-    if (kn <= c1) issue(kn, kn_lds, vn_lds, sn_lds);
+    const bool more = kn <= c1;
+    if (more && wave == 0) vec_async_load(sn_lds, segk_b, kn * BK, p.Sk, lane);
 
     bf16x8 dsb[4];
 #pragma unroll
@@ -627,11 +713,16 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
       f32x16 sacc = f32x16{0}, pacc = f32x16{0};
       const int krow = 32 * sub + kperm(col);
       __builtin_amdgcn_s_setprio(1);
+      if (sub == 0 && more) {  // the next tile's K and V loads go out between these MFMAs
+        sdp_chain(sacc, pacc, kb_lds, vb_lds, krow, hf, qreg, greg,
+                  PairDma(Kh, Vh, kn * BK, p.Sk, kn_lds, vn_lds, wave, lane));
+      } else {
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const int off = tile_off(krow, 16 * s + 8 * hf);
-        sacc = mfma32(lds_load8(kb_lds + off), qreg[s], sacc);
-        pacc = mfma32(lds_load8(vb_lds + off), greg[s], pacc);
+        for (int s = 0; s < D / 16; ++s) {
+          const int off = tile_off(krow, 16 * s + 8 * hf);
+          sacc = mfma32(lds_load8(kb_lds + off), qreg[s], sacc);
+          pacc = mfma32(lds_load8(vb_lds + off), greg[s], pacc);
+        }
       }
       __builtin_amdgcn_s_setprio(0);
       if (st == LWM_TILE_PARTIAL) {
@@ -740,7 +831,8 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
   const int rest = idx / p.H;
   const int kt = rest % nkt;  // early keys see the most queries under the causal mask
   const int b = rest / nkt;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, col = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t bh = int64_t(b) * p.H + h;
   const uint16_t* Qh = Q + bh * p.Sq * D;
   const uint16_t* Gh = dO + bh * p.Sq * D;
@@ -780,12 +872,15 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
     dvacc[i] = f32x16{0};
   }
 
-  auto issue = [&](int qb, uint16_t* qd, uint16_t* gd, float* rd) {
-    tile_async_load(qd, Qh, qb * TB, p.Sq, wave, lane);
-    tile_async_load(gd, Gh, qb * TB, p.Sq, wave, lane);
+  auto issue_rows = [&](int qb, float* rd) {
     if (wave == 0) vec_async_load(rd, lse_h, qb * TB, p.Sq, lane);
     if (wave == 1) vec_async_load(rd + TB, dl_h, qb * TB, p.Sq, lane);
     if (wave == 2) vec_async_load(rd + 2 * TB, segq_b, qb * TB, p.Sq, lane);
+  };
+  auto issue = [&](int qb, uint16_t* qd, uint16_t* gd, float* rd) {
+    tile_async_load(qd, Qh, qb * TB, p.Sq, wave, lane);
+    tile_async_load(gd, Gh, qb * TB, p.Sq, wave, lane);
+    issue_rows(qb, rd);
   };
 
   int qb = 0, w0 = 0, w1 = -1;
@@ -795,7 +890,8 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
     const int qn = next_live_lds(stat_lds, w0, qb + 1, w1);
     wait_vmem();
     __syncthreads();
-    if (qn <= w1) issue(qn, qn_lds, gn_lds, rn_lds);
+    const bool more = qn <= w1;
+    if (more) issue_rows(qn, rn_lds);
 
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -810,11 +906,16 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
         for (int j = 0; j < 8; ++j) pacc[8 * a + j] = ndl[j];
       }
       const int qrow = 32 * sub + kperm(col);
+      if (sub == 0 && more) {  // the next tile's Q and dO loads go out between these MFMAs
+        sdp_chain(sacc, pacc, qb_lds, gb_lds, qrow, hf, kreg, vreg,
+                  PairDma(Qh, Gh, qn * TB, p.Sq, qn_lds, gn_lds, wave, lane));
+      } else {
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const int off = tile_off(qrow, 16 * s + 8 * hf);
-        sacc = mfma32(lds_load8(qb_lds + off), kreg[s], sacc);
-        pacc = mfma32(lds_load8(gb_lds + off), vreg[s], pacc);
+        for (int s = 0; s < D / 16; ++s) {
+          const int off = tile_off(qrow, 16 * s + 8 * hf);
+          sacc = mfma32(lds_load8(qb_lds + off), kreg[s], sacc);
+          pacc = mfma32(lds_load8(gb_lds + off), vreg[s], pacc);
+        }
       }
       if (st == LWM_TILE_PARTIAL) {
         // hidden scores become -inf, so their probabilities come out as exactly 0; keys
