@@ -30,9 +30,14 @@ COMMON_FLAGS = [
 ]
 
 
+# attn_bf16.hip: MFMAs in the VGPR form, so that score accumulators feed the softmax without
+# AGPR copies; the dK/dV kernel keeps its accumulators in AGPRs through asm constraints.
+SOURCE_FLAGS = {"attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS]
+    cmd = [HIPCC, *COMMON_FLAGS, *SOURCE_FLAGS.get(src, [])]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]

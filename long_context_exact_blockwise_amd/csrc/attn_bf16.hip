@@ -806,6 +806,22 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
     }
 }
 
+// dK/dV accumulation into AGPRs.  The dK/dV kernel needs more than 256 registers; built
+// with MFMAs in VGPR form (see build.py), its score and dP accumulators sit in VGPRs that the
+// softmax reads directly, while the constraint here keeps the long-lived dK/dV accumulators
+// in AGPRs.  The compiler's hazard checks do not see inside asm, so the asm carries them:
+// s_nop 1 gives the two wait states an MFMA needs after a VALU write of its A/B operand
+// (ds_read results are covered by the compiler's lgkmcnt waits); mfma_agpr_fence covers the
+// AGPR writes before the first MFMA and the MFMA results before the first AGPR read.
+__device__ __forceinline__ void mfma32_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_agpr_fence(f32x16* x, f32x16* y) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]), "+a"(y[0]), "+a"(y[1]), "+a"(y[2]),
+                 "+a"(y[3]));
+}
+
 // dK, dV: key-major.  Workgroup = 128 keys (32 per wave) held in registers; query tiles of
 // 64 stream through LDS.  Per 32-query half: S = Q K^T, dP = dO V^T, P = exp(S - LSE),
 // dS = P (dP - Delta), dV^T += dO^T P, dK^T += Q^T dS (dO^T, Q^T read transposed).
@@ -871,6 +887,8 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
     dkacc[i] = f32x16{0};
     dvacc[i] = f32x16{0};
   }
+  static_assert(D / 32 == 4, "mfma_agpr_fence takes four accumulators of each kind");
+  mfma_agpr_fence(dkacc, dvacc);
 
   auto issue_rows = [&](int qb, float* rd) {
     if (wave == 0) vec_async_load(rd, lse_h, qb * TB, p.Sq, lane);
@@ -955,8 +973,8 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
         const int ks = 2 * sub + a;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          dvacc[db] = mfma32(lds_load_tr8(gb_lds, 16 * ks, 32 * db, lane), pb[a], dvacc[db]);
-          dkacc[db] = mfma32(lds_load_tr8(qb_lds, 16 * ks, 32 * db, lane), dsb[a], dkacc[db]);
+          mfma32_agpr(dvacc[db], lds_load_tr8(gb_lds, 16 * ks, 32 * db, lane), pb[a]);
+          mfma32_agpr(dkacc[db], lds_load_tr8(qb_lds, 16 * ks, 32 * db, lane), dsb[a]);
         }
       }
     }
@@ -977,6 +995,7 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
       step(q_lds0 + 2 * kTileElems, g_lds0 + 2 * kTileElems, row_lds + 3 * TB, q_lds0, g_lds0, row_lds);
     }
   }
+  mfma_agpr_fence(dkacc, dvacc);
   if (!klive) return;
   uint16_t* ko = dK + k64 * D;
   uint16_t* vo = dV + k64 * D;
