@@ -911,35 +911,35 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
     const bool more = qn <= w1;
     if (more) issue_rows(qn, rn_lds);
 
+    // both 32-row halves' S and dP first (the next tile's loads spread between the first
+    // half's MFMAs), then the masks, the softmax of both halves and their dV/dK updates
+    f32x16 sacc[2], pacc[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       // dP starts from -Delta of each query row (slot 8a + j holds row 32 sub + 16a + 8hf + j),
       // so the products deliver dP - Delta directly
-      f32x16 sacc = f32x16{0}, pacc;
+      sacc[sub] = f32x16{0};
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         float ndl[8];
         lds_load_f8(rb_lds + TB + 32 * sub + 16 * a + 8 * hf, ndl);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pacc[8 * a + j] = ndl[j];
+        for (int j = 0; j < 8; ++j) pacc[sub][8 * a + j] = ndl[j];
       }
-      const int qrow = 32 * sub + kperm(col);
-      if (sub == 0 && more) {  // the next tile's Q and dO loads go out between these MFMAs
-        sdp_chain(sacc, pacc, qb_lds, gb_lds, qrow, hf, kreg, vreg,
-                  PairDma(Qh, Gh, qn * TB, p.Sq, qn_lds, gn_lds, wave, lane));
-      } else {
+    }
+    if (more)
+      sdp_chain(sacc[0], pacc[0], qb_lds, gb_lds, kperm(col), hf, kreg, vreg,
+                PairDma(Qh, Gh, qn * TB, p.Sq, qn_lds, gn_lds, wave, lane));
+    else
+      sdp_chain(sacc[0], pacc[0], qb_lds, gb_lds, kperm(col), hf, kreg, vreg, NoDma{});
+    sdp_chain(sacc[1], pacc[1], qb_lds, gb_lds, 32 + kperm(col), hf, kreg, vreg, NoDma{});
+    if (st == LWM_TILE_PARTIAL) {
+      // hidden scores become -inf, so their probabilities come out as exactly 0; keys past Sk
+      // carry sk = -2 and see no row
+      int rlo, rhi;
+      row_window(qb * TB + 8 * hf, key, dpos, p.Sq, p.causal, sk >= 0, rlo, rhi);
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          const int off = tile_off(qrow, 16 * s + 8 * hf);
-          sacc = mfma32(lds_load8(qb_lds + off), kreg[s], sacc);
-          pacc = mfma32(lds_load8(gb_lds + off), vreg[s], pacc);
-        }
-      }
-      if (st == LWM_TILE_PARTIAL) {
-        // hidden scores become -inf, so their probabilities come out as exactly 0; keys
-        // past Sk carry sk = -2 and see no row
-        int rlo, rhi;
-        row_window(qb * TB + 8 * hf, key, dpos, p.Sq, p.causal, sk >= 0, rlo, rhi);
+      for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
           int sq8[8];
@@ -948,36 +948,33 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
           for (int j = 0; j < 8; ++j) {
             const int o = 32 * sub + 16 * a + j;
             const bool vis = (sq8[j] == sk) & (o >= rlo) & (o <= rhi);
-            sacc[8 * a + j] = vis ? sacc[8 * a + j] : -INFINITY;
+            sacc[sub][8 * a + j] = vis ? sacc[sub][8 * a + j] : -INFINITY;
           }
         }
-      }
-      bf16x8 pb[2], dsb[2];
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const int qbase = 32 * sub + 16 * a + 8 * hf;  // 8 consecutive local query rows
-        float lsev[8];
-        lds_load_f8(rb_lds + qbase, lsev);
-        float pv[8], ds[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int i = 8 * a + j;
-          pv[j] = fast_exp2(fmaf(sacc[i], c, -lsev[j]));
-          ds[j] = pv[j] * pacc[i];
-        }
-        pb[a] = to_bf16x8(pv);
-        dsb[a] = to_bf16x8(ds);
-      }
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const int ks = 2 * sub + a;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          mfma32_agpr(dvacc[db], lds_load_tr8(gb_lds, 16 * ks, 32 * db, lane), pb[a]);
-          mfma32_agpr(dkacc[db], lds_load_tr8(qb_lds, 16 * ks, 32 * db, lane), dsb[a]);
-        }
-      }
     }
+    bf16x8 pb[4], dsb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int qbase = 16 * ks + 8 * hf;  // 8 consecutive local query rows
+      float lsev[8];
+      lds_load_f8(rb_lds + qbase, lsev);
+      float pv[8], ds[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = 8 * (ks & 1) + j;
+        pv[j] = fast_exp2(fmaf(sacc[ks >> 1][i], c, -lsev[j]));
+        ds[j] = pv[j] * pacc[ks >> 1][i];
+      }
+      pb[ks] = to_bf16x8(pv);
+      dsb[ks] = to_bf16x8(ds);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        mfma32_agpr(dvacc[db], lds_load_tr8(gb_lds, 16 * ks, 32 * db, lane), pb[ks]);
+        mfma32_agpr(dkacc[db], lds_load_tr8(qb_lds, 16 * ks, 32 * db, lane), dsb[ks]);
+      }
     qb = qn;
   };
 
