@@ -901,11 +901,16 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
     issue_rows(qb, rd);
   };
 
-  int qb = 0, w0 = 0, w1 = -1;
+  // st_c and qn_c: the status of tile qb and the next live tile after it, read one step
+  // ahead, so that no LDS round trip sits between two steps
+  int qb = 0, w0 = 0, w1 = -1, st_c = 0, qn_c = 0;
   auto step = [&](const uint16_t* qb_lds, const uint16_t* gb_lds, const float* rb_lds,
                   uint16_t* qn_lds, uint16_t* gn_lds, float* rn_lds) {
-    const int st = uniform(stat_lds[qb - w0]);
-    const int qn = next_live_lds(stat_lds, w0, qb + 1, w1);
+    const int st = st_c;
+    const int qn = qn_c;
+    // the next step's: statuses of tiles qn and qn + 1 (indices kept inside the chunk)
+    const int st_n = stat_lds[min(qn, w1) - w0];
+    const int s_after = stat_lds[min(qn + 1, w1) - w0];
     wait_vmem();
     __syncthreads();
     const bool more = qn <= w1;
@@ -952,6 +957,19 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
           }
         }
     }
+    // dV/dK operand reads (transposed dO and Q tiles) run kAhead MFMAs ahead of their use in a
+    // fixed order: at one wave per SIMD the scheduler, which cannot see into the asm MFMAs,
+    // placed them too late.  The first ones go out before the softmax.  MFMA m updates dV
+    // (even m) or dK (odd m) for key step ks = m / 8 and column block db = (m / 2) % 4.
+    constexpr int kAhead = 6;
+    bf16x8 op[32];
+    auto opread = [&](int m) {
+      const int ks = m >> 3, db = (m >> 1) & 3;
+      op[m] = lds_load_tr8((m & 1) ? qb_lds : gb_lds, 16 * ks, 32 * db, lane);
+    };
+#pragma unroll
+    for (int m = 0; m < kAhead; ++m) opread(m);
+    __builtin_amdgcn_sched_barrier(0);
     bf16x8 pb[4], dsb[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -968,13 +986,20 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
       pb[ks] = to_bf16x8(pv);
       dsb[ks] = to_bf16x8(ds);
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        mfma32_agpr(dvacc[db], lds_load_tr8(gb_lds, 16 * ks, 32 * db, lane), pb[ks]);
-        mfma32_agpr(dkacc[db], lds_load_tr8(qb_lds, 16 * ks, 32 * db, lane), dsb[ks]);
-      }
+    for (int m = 0; m < 32; ++m) {
+      const int ks = m >> 3, db = (m >> 1) & 3;
+      if (m & 1)
+        mfma32_agpr(dkacc[db], op[m], dsb[ks]);
+      else
+        mfma32_agpr(dvacc[db], op[m], pb[ks]);
+      if (m + kAhead < 32) opread(m + kAhead);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    st_c = uniform(st_n);
+    qn_c = (qn + 1 <= w1 && uniform(s_after) == LWM_TILE_SKIP) ? next_live_lds(stat_lds, w0, qn + 2, w1)
+                                                                : qn + 1;
     qb = qn;
   };
 
@@ -984,6 +1009,10 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
     stage_status_cols(stat_lds, stb, t.nkb, c0, has_c1, w0, w1, tid);
     __syncthreads();
     qb = next_live_lds(stat_lds, w0, w0, w1);
+    if (qb <= w1) {
+      st_c = uniform(stat_lds[qb - w0]);
+      qn_c = next_live_lds(stat_lds, w0, qb + 1, w1);
+    }
     // unrolled by two, so every LDS address is a register plus a constant offset
     if (qb <= w1) issue(qb, q_lds0, g_lds0, row_lds);
     while (qb <= w1) {
