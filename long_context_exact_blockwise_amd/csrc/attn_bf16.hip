@@ -201,11 +201,10 @@ __device__ __forceinline__ void vec_async_load(void* dst, const void* src, int r
 }
 
 // The same loads for a pair of tiles (K and V, or Q and dO), one instruction per call:
-// 0-3 fill the first tile, 4-7 the second.  Issued all at once after the barrier, the eight
-// instructions of each of the four waves queue behind the buffer unit, which moves one
-// 1 KiB instruction every 16 cycles or so, and the waves stall for hundreds of cycles
-// before their first MFMA; issued one at a time between the score MFMAs, they drain
-// while the matrix pipe works.
+// 0-3 fill the first tile, 4-7 the second.  Issued all at once after the barrier, the 32
+// instructions of a workgroup's four waves queue in the buffer unit and each wave stalls
+// before its first MFMA (in-kernel timestamps of the forward: 450-800 cycles); issued one
+// at a time between the score MFMAs, they drain while the matrix pipe works.
 struct PairDma {
   const uint16_t* a;
   const uint16_t* b;
