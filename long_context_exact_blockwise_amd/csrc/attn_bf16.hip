@@ -711,7 +711,6 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
     for (int sub = 0; sub < 2; ++sub) {
       f32x16 sacc = f32x16{0}, pacc = f32x16{0};
       const int krow = 32 * sub + kperm(col);
-      __builtin_amdgcn_s_setprio(1);
       if (sub == 0 && more) {  // the next tile's K and V loads go out between these MFMAs
         sdp_chain(sacc, pacc, kb_lds, vb_lds, krow, hf, qreg, greg,
                   PairDma(Kh, Vh, kn * BK, p.Sk, kn_lds, vn_lds, wave, lane));
@@ -723,7 +722,6 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
           pacc = mfma32(lds_load8(vb_lds + off), greg[s], pacc);
         }
       }
-      __builtin_amdgcn_s_setprio(0);
       if (st == LWM_TILE_PARTIAL) {
         // hidden scores become -inf, so their probabilities come out as exactly 0
         const int lim = key_limit(kt * BK + 8 * hf, qrow, dpos, p.Sk, p.causal, sq >= 0);
@@ -768,13 +766,11 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
       // of score registers, which does not fit beside two waves per SIMD
       __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 2; ks < BK / 16; ++ks)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
         dqacc[db] = mfma32(lds_load_tr8(kb_lds, 16 * ks, 32 * db, lane), dsb[ks], dqacc[db]);
-    __builtin_amdgcn_s_setprio(0);
     kt = kn;
   };
 
