@@ -8,6 +8,7 @@ import pytest
 
 import lwm_inputs as li
 from oracle import attention as A
+from oracle import table as otab
 import test_oracle_pins as pins
 from gpu_helpers import (TOL_GRAD, TOL_LSE, TOL_O, f64, host_f64, max_abs, rel_errors, say,
                          seg_dev, to_dev)
@@ -26,6 +27,11 @@ def make_case(seed, B, H, Sq, Sk, D, dtype, layout="packed", q_off=0, k_off=0, p
         ids = np.zeros(total, np.int32)
     elif layout == "packed":
         ids = pins.random_layout(rng, total, allow_padding=pad)
+    elif layout.startswith("alternating"):
+        # ids 0, 1, 0, 1, ... in runs of `run` tokens: a sample's tokens are not contiguous, so
+        # SKIP tiles sit between live tiles of a row's (and a column's) range
+        run = int(layout.split("_")[1])
+        ids = ((np.arange(total) // run) % 2).astype(np.int32)
     else:
         raise ValueError(layout)
     seg_q = np.stack([ids[q_off:q_off + Sq]] * B)
@@ -56,6 +62,8 @@ CASES = [
     ("short_q", 7, 1, 3, 37, 300, "packed", 263, 0, True, False),
     ("one_row", 8, 1, 1, 1, 1, "single", 0, 0, True, False),
     ("few_keys", 9, 1, 2, 130, 3, "single", 0, 0, False, False),
+    ("alternating_tiles", 10, 1, 2, 1024, 1024, "alternating_128", 0, 0, True, False),
+    ("alternating_ragged", 11, 1, 2, 900, 900, "alternating_100", 0, 0, True, False),
 ]
 
 
@@ -65,6 +73,13 @@ def test_bf16_forward_and_backward(case):
     D = 128
     say(f"bf16 case {name}: B={B} H={H} Sq={Sq} Sk={Sk} offs={q_off},{k_off} causal={causal}")
     x, seg_q, seg_k = make_case(seed, B, H, Sq, Sk, D, "bf16", layout, q_off, k_off, pad)
+    if layout.startswith("alternating"):
+        # the layout does what it is for: SKIP tiles between live tiles of a row and a column
+        st = otab.classify(seg_q[0], seg_k[0], 64, 64, q_off, k_off, causal)
+        def gap(v):
+            live = np.nonzero(v != otab.SKIP)[0]
+            return live.size > 1 and np.any(v[live[0]:live[-1] + 1] == otab.SKIP)
+        assert any(gap(r) for r in st) and any(gap(c) for c in st.T)
     scale = 1 / math.sqrt(D)
     o_ref, lse_ref, (dq_ref, dk_ref, dv_ref) = run_oracle(x, seg_q, seg_k, "bf16", scale, causal,
                                                           q_off, k_off)
