@@ -368,17 +368,28 @@ __device__ __forceinline__ void fwd_bf16_body(AttnParams p, TableView t, int mod
 
   // One key tile: wait for its loads, then S^T (starting the next tile's loads into the
   // other buffers), mask, online softmax and O^T += V^T P^T.
-  int kt = 0, c0 = 0, c1 = -1;
+  // st_c and kn_c: the status of tile kt and the next live tile after it, read one step
+  // ahead, so that no LDS round trip sits between two steps
+  int kt = 0, c0 = 0, c1 = -1, st_c = 0, kn_c = 0;
   auto step = [&](const uint16_t* kb_lds, const uint16_t* vb_lds, const int32_t* sb_lds,
                   uint16_t* kn_lds, uint16_t* vn_lds, int32_t* sn_lds) {
-    const int st = uniform(stat_lds[kt - c0]);
-    const int kn = next_live_lds(stat_lds, c0, kt + 1, c1);
+    const int st = st_c;
+    const int kn = kn_c;
+    // the next step's: statuses of tiles kn and kn + 1 (indices kept inside the chunk)
+    const int st_n = stat_lds[min(kn, c1) - c0];
+    const int s_after = stat_lds[min(kn + 1, c1) - c0];
+    auto advance = [&]() {
+      st_c = uniform(st_n);
+      kn_c = (kn + 1 <= c1 && uniform(s_after) == LWM_TILE_SKIP) ? next_live_lds(stat_lds, c0, kn + 2, c1)
+                                                                 : kn + 1;
+      kt = kn;
+    };
     wait_vmem();
     __syncthreads();
     const bool more = kn <= c1;
     if (!wave_live) {
       if (more) issue(kn, kn_lds, vn_lds, sn_lds);
-      kt = kn;
+      advance();
       return;
     }
 
@@ -454,7 +465,7 @@ __device__ __forceinline__ void fwd_bf16_body(AttnParams p, TableView t, int mod
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 2);
-    kt = kn;
+    advance();
   };
 
   for (c0 = lo; c0 <= hi; c0 += kStatChunk) {
@@ -463,6 +474,10 @@ __device__ __forceinline__ void fwd_bf16_body(AttnParams p, TableView t, int mod
     stage_status_rows(stat_lds, st0, st1, has_r1, c0, c1, tid);
     __syncthreads();
     kt = next_live_lds(stat_lds, c0, c0, c1);
+    if (kt <= c1) {
+      st_c = uniform(stat_lds[kt - c0]);
+      kn_c = next_live_lds(stat_lds, c0, kt + 1, c1);
+    }
     if (kt <= c1) issue(kt, k_lds, v_lds, segk_lds);
     while (kt <= c1) {
       step(k_lds, v_lds, segk_lds, k_lds + kTileElems, v_lds + kTileElems, segk_lds + BK);
