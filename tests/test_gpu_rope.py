@@ -16,7 +16,7 @@ import pytest
 import lwm_inputs as li
 from oracle import attention as A
 from oracle import rope as R
-from gpu_helpers import TOL_GRAD, TOL_LSE, TOL_O, f64, host_f64, max_abs, say, seg_dev, to_dev
+from gpu_helpers import TOL_GRAD, TOL_LSE, TOL_O, check_grad, f64, host_f64, max_abs, say, seg_dev, to_dev
 from test_gpu_small import make_case
 
 pytestmark = pytest.mark.gpu
@@ -128,7 +128,8 @@ def test_attention_with_rope_matches_oracle(case):
     eq, ek, ev = max_abs(f64(dq), dq_ref), max_abs(f64(dk), dk_ref), max_abs(f64(dv), dv_ref)
     say(f"  max-abs O {eo:.2e} LSE {el:.2e} dQ {eq:.2e} dK {ek:.2e} dV {ev:.2e}")
     assert eo <= TOL_O[dt] and el <= TOL_LSE
-    assert max(eq, ek, ev) <= TOL_GRAD[dt]
+    for n, g, r in (("dQ", dq, dq_ref), ("dK", dk, dk_ref), ("dV", dv, dv_ref)):
+        check_grad(n, f64(g), r, dt)
 
 
 def test_rope_packed_128k_sampled_rows():

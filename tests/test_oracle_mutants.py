@@ -194,7 +194,68 @@ def test_loss_pins_catch_mutant(idx, monkeypatch):
             check()
 
 
+from oracle import table as T
+
+_orig_forward = A.forward
+_orig_backward = A.backward
+_orig_ranges = T.ranges_from_status
+
+
+def fwd_batch_mask_of_row0(q, k, v, seg_q, seg_k, scale, causal=True, q_offset=0, k_offset=0):
+    # every batch row attends under the first row's mask
+    sq = np.repeat(np.asarray(seg_q)[:1], len(seg_q), axis=0)
+    sk = np.repeat(np.asarray(seg_k)[:1], len(seg_k), axis=0)
+    return _orig_forward(q, k, v, sq, sk, scale, causal, q_offset, k_offset)
+
+
+def bwd_batch_do_of_row0(q, k, v, do, seg_q, seg_k, scale, causal=True, q_offset=0, k_offset=0):
+    # the first row's upstream gradient reused for every batch row
+    do0 = np.repeat(np.asarray(do)[:1], len(do), axis=0)
+    return _orig_backward(q, k, v, do0, seg_q, seg_k, scale, causal, q_offset, k_offset)
+
+
+def ranges_full_as_skip(status):
+    st = np.where(np.asarray(status) == T.FULL, T.SKIP, status).astype(np.uint8)
+    return _orig_ranges(st)
+
+
+def ranges_last_one_short(status):
+    q, k = _orig_ranges(status)
+    q, k = q.copy(), k.copy()
+    q[:, 1] = np.where(q[:, 1] > q[:, 0], q[:, 1] - 1, q[:, 1])
+    k[:, 1] = np.where(k[:, 1] > k[:, 0], k[:, 1] - 1, k[:, 1])
+    return q, k
+
+
+def ranges_empty_as_zero(status):
+    q, k = _orig_ranges(status)
+    q, k = q.copy(), k.copy()
+    q[q[:, 1] < q[:, 0]] = 0
+    k[k[:, 1] < k[:, 0]] = 0
+    return q, k
+
+
+TABLE_MUTANTS = [
+    ("ranges_from_status", ranges_full_as_skip, [lambda: pins.test_ranges_from_status_by_scanning(0)]),
+    ("ranges_from_status", ranges_last_one_short, [pins.test_tiny_ranges_match_hand_derivation]),
+    ("ranges_from_status", ranges_empty_as_zero, [lambda: pins.test_ranges_from_status_by_scanning(1)]),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(TABLE_MUTANTS)))
+def test_table_pins_catch_mutant(idx, monkeypatch):
+    name, mutant, checks = TABLE_MUTANTS[idx]
+    monkeypatch.setattr(T, name, mutant)
+    for check in checks:
+        with pytest.raises(AssertionError):
+            check()
+
+
 MUTANTS = [
+    ("forward", fwd_batch_mask_of_row0,
+     [pins.test_batch_rows_equal_single_row_calls, pins.test_batch_matches_torch_sdpa_per_row_masks]),
+    ("backward", bwd_batch_do_of_row0,
+     [pins.test_batch_rows_equal_single_row_calls, pins.test_batch_matches_torch_sdpa_per_row_masks]),
     ("visibility", vis_strict_causal,
      [lambda: pins.test_brute_force_tiny(0), lambda: pins.test_matches_torch_sdpa_float64("single_causal")]),
     ("visibility", vis_ignores_segments,

@@ -295,8 +295,22 @@ def load_golden_table():
             if line.startswith("pairs"):
                 pairs = int(line.split()[1])
                 continue
+            if line.startswith(("q_range", "k_range")):
+                continue
             rows.append([codes[c] for c in line.split()])
     return np.array(rows, np.uint8), pairs
+
+
+def load_golden_ranges():
+    """(q_range [nqb,2], k_range [nkb,2]) as read off the hand-derived table."""
+    out = {}
+    with open(os.path.join(GOLDEN, "tiny_packed_table.txt")) as f:
+        for line in f:
+            if line.startswith(("q_range", "k_range")):
+                name, rest = line.split(None, 1)
+                out[name] = np.array([[int(a) for a in part.split()] for part in rest.split("|")],
+                                     np.int32)
+    return out["q_range"], out["k_range"]
 
 
 def test_tiny_table_matches_hand_derivation():
@@ -307,6 +321,66 @@ def test_tiny_table_matches_hand_derivation():
     assert int((st == table.PARTIAL).sum()) == 7 and int((st == table.FULL).sum()) == 0
     assert table.visible_pairs(sq, sk) == pairs == 11356
     assert pairs * 4 * 64 == 2_907_136
+
+
+def test_tiny_ranges_match_hand_derivation():
+    """The per-row and per-column ranges of live tiles of the tiny packed table, read off by
+    hand (tests/golden/tiny_packed_table.txt), equal the oracle's ranges_from_status."""
+    w, q, k, v, do, sq, sk = tiny_case()
+    q_gold, k_gold = load_golden_ranges()
+    q_rng, k_rng = table.ranges_from_status(table.classify(sq, sk, 64, 64))
+    assert np.array_equal(q_rng, q_gold)
+    assert np.array_equal(k_rng, k_gold)
+
+
+def _scan_ranges(status):
+    """Independent evaluation by plain loops: walk each row (column) from both ends until a
+    tile that is not SKIP is met; (0, -1) when the walk from the front runs off the end."""
+    nqb, nkb = status.shape
+
+    def walk(cells):
+        n = len(cells)
+        first = 0
+        while first < n and cells[first] == table.SKIP:
+            first += 1
+        if first == n:
+            return (0, -1)
+        last = n - 1
+        while cells[last] == table.SKIP:
+            last -= 1
+        return (first, last)
+
+    q = [walk([int(status[a, c]) for c in range(nkb)]) for a in range(nqb)]
+    k = [walk([int(status[a, c]) for a in range(nqb)]) for c in range(nkb)]
+    return np.array(q, np.int32).reshape(nqb, 2), np.array(k, np.int32).reshape(nkb, 2)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_ranges_from_status_by_scanning(seed):
+    """Random status matrices (all three codes, whole empty rows and columns, 1 x n and n x 1
+    shapes) and tables of random packed layouts with padding: ranges_from_status equals a
+    scan from both ends of every row and column."""
+    rng = np.random.default_rng(100 + seed)
+    shapes = [(1, 7), (9, 1), (5, 5), (int(rng.integers(2, 12)), int(rng.integers(2, 12)))]
+    mats = []
+    for shp in shapes:
+        st = rng.choice([table.SKIP, table.PARTIAL, table.FULL], size=shp,
+                        p=[0.6, 0.25, 0.15]).astype(np.uint8)
+        if shp[0] > 2:
+            st[rng.integers(0, shp[0])] = table.SKIP      # an empty row
+        if shp[1] > 2:
+            st[:, rng.integers(0, shp[1])] = table.SKIP   # an empty column
+        mats.append(st)
+    S = int(rng.integers(100, 400))
+    ids = random_layout(rng, S, allow_padding=True)
+    ids[: int(rng.integers(0, 40))] = -1                  # leading padding: empty query blocks
+    mats.append(table.classify(ids, ids, 16, 32))
+    mats.append(table.classify(ids[:S // 2], ids, 32, 16, q_offset=S - S // 2, k_offset=0))
+    for st in mats:
+        q_rng, k_rng = table.ranges_from_status(st)
+        q_ref, k_ref = _scan_ranges(st)
+        assert np.array_equal(q_rng, q_ref), st
+        assert np.array_equal(k_rng, k_ref), st
 
 
 # --------------------------------------------------------------------------------------
@@ -373,6 +447,88 @@ def test_matches_torch_sdpa_float64(layout):
     m = torch.tensor(A.visibility(seg, seg, causal=causal))
     tl = torch.logsumexp(s.masked_fill(~m, float("-inf")), dim=-1)
     assert np.max(np.abs(lse - tl.numpy())) < 1e-12
+
+
+# --------------------------------------------------------------------------------------
+# 10. batches: each batch row with its own packing is its own instance
+# --------------------------------------------------------------------------------------
+
+def _batch_case(seed=29, B=3, H=2, Sq=70, Sk=90, D=8, q_off=20, k_off=0):
+    rng = np.random.default_rng(seed)
+    total = max(q_off + Sq, k_off + Sk)
+    layouts = [random_layout(rng, total, allow_padding=False),
+               random_layout(rng, total, allow_padding=True),
+               np.zeros(total, np.int32)]
+    layouts[0] = layouts[0] + 3                     # ids need not start at 0
+    seg_q = np.stack([l[q_off:q_off + Sq] for l in layouts[:B]]).astype(np.int32)
+    seg_k = np.stack([l[k_off:k_off + Sk] for l in layouts[:B]]).astype(np.int32)
+    q = rng.standard_normal((B, H, Sq, D))
+    k, v = rng.standard_normal((2, B, H, Sk, D))
+    do = rng.standard_normal((B, H, Sq, D))
+    return q, k, v, do, seg_q, seg_k, q_off, k_off
+
+
+def test_batch_rows_equal_single_row_calls():
+    """Three batch rows with different layouts (packed, padded, one segment) and their own
+    values: the batched forward and backward equal each row run alone as a batch of one."""
+    q, k, v, do, seg_q, seg_k, q_off, k_off = _batch_case()
+    assert not np.array_equal(seg_q[0], seg_q[1]) and not np.array_equal(seg_q[1], seg_q[2])
+    scale = 0.35
+    o, lse = A.forward(q, k, v, seg_q, seg_k, scale, True, q_off, k_off)
+    dq, dk, dv = A.backward(q, k, v, do, seg_q, seg_k, scale, True, q_off, k_off)
+    for b in range(q.shape[0]):
+        sl = slice(b, b + 1)
+        ob, lb = A.forward(q[sl], k[sl], v[sl], seg_q[sl], seg_k[sl], scale, True, q_off, k_off)
+        gb = A.backward(q[sl], k[sl], v[sl], do[sl], seg_q[sl], seg_k[sl], scale, True, q_off, k_off)
+        assert np.array_equal(o[sl], ob) and np.array_equal(lse[sl], lb)
+        for g, r in zip((dq, dk, dv), gb):
+            assert np.array_equal(g[sl], r)
+
+
+def test_batch_matches_torch_sdpa_per_row_masks():
+    """The same batch against torch's float64 scaled-dot-product attention with a boolean
+    mask per batch row (built here from the ids and global positions), forward and
+    autograd; rows that see no key (padding) are checked to give O = 0 and LSE = -inf."""
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+
+    q, k, v, do, seg_q, seg_k, q_off, k_off = _batch_case()
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    scale = 0.35
+    o, lse = A.forward(q, k, v, seg_q, seg_k, scale, True, q_off, k_off)
+    dq, dk, dv = A.backward(q, k, v, do, seg_q, seg_k, scale, True, q_off, k_off)
+    allowed = np.zeros((B, 1, Sq, Sk), bool)
+    for b in range(B):
+        for i in range(Sq):
+            for j in range(Sk):
+                allowed[b, 0, i, j] = (seg_q[b, i] >= 0 and seg_q[b, i] == seg_k[b, j]
+                                       and k_off + j <= q_off + i)
+    live = allowed.any(axis=-1)[:, 0]                        # [B, Sq]
+    assert (~live).any() and live.any()
+    # torch gives NaN on rows with no visible key; feed it a harmless key for them and
+    # zero their upstream gradient, then compare live rows only
+    safe = allowed.copy()
+    safe[..., 0] |= ~live[:, None, :]
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    to = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.tensor(safe), scale=scale)
+    to.backward(torch.tensor(do * live[:, None, :, None]))
+    lv = live[:, None, :, None].repeat(H, 1)
+    assert np.max(np.abs(np.where(lv, o - to.detach().numpy(), 0.0))) < 1e-12
+    assert np.all(o[~lv.repeat(D, -1)] == 0.0)
+    s = torch.tensor(q) @ torch.tensor(k).transpose(-1, -2) * scale
+    tl = torch.logsumexp(s.masked_fill(~torch.tensor(safe), float("-inf")), dim=-1).numpy()
+    l2 = live[:, None, :].repeat(H, 1)
+    assert np.max(np.abs(np.where(l2, lse - tl, 0.0))) < 1e-12
+    assert np.all(lse[~l2] == -np.inf)
+    # gradients: rows that see nothing contribute nothing, so the oracle run on the same
+    # upstream gradient restricted to live rows must match torch everywhere
+    dq2, dk2, dv2 = A.backward(q, k, v, do * live[:, None, :, None], seg_q, seg_k, scale, True,
+                               q_off, k_off)
+    for g, tg in ((dq2, tq.grad), (dk2, tk.grad), (dv2, tv.grad)):
+        assert np.max(np.abs(g - tg.numpy())) < 1e-12
+    assert np.array_equal(dk, dk2) and np.array_equal(dv, dv2)
+    assert np.max(np.abs(dq - dq2)) == 0.0
 
 
 # --------------------------------------------------------------------------------------
