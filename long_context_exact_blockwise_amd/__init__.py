@@ -135,6 +135,50 @@ def _dtype_code(dtype) -> int:
     raise ValueError(f"unsupported dtype {dtype}")
 
 
+def _torch_dtype(code: int):
+    import torch
+
+    return {LWM_BF16: torch.bfloat16, LWM_F32: torch.float32}.get(int(code))
+
+
+def _expect(t, numel: int, dtype, name: str):
+    """Raise ValueError unless t (when given) holds exactly `numel` elements of `dtype`: the
+    C entry points take raw pointers and cannot see a buffer's size."""
+    if t is None:
+        return
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"lwm_attn: {name} has dtype {t.dtype}, expected {dtype}")
+    if t.numel() != numel:
+        raise ValueError(f"lwm_attn: {name} has {t.numel()} elements, expected {numel}")
+
+
+def _expect_attention(desc: "Desc", q=None, k=None, v=None, seg_q=None, seg_k=None, table=None,
+                      qlike=(), klike=(), rowf=(), accs=()):
+    """Sizes and dtypes of attention buffers against desc: Q-shaped [B,H,Sq,D] and K-shaped
+    [B,H,Sk,D] in the desc dtype, float32 per-row [B,H,Sq] and accumulators [B,H,Sq,D],
+    int32 segment ids [B,Sq] / [B,Sk], and a table of at least the size query's bytes."""
+    import torch
+
+    dt = _torch_dtype(desc.dtype)
+    nq = desc.B * desc.H * desc.Sq * desc.D
+    nk = desc.B * desc.H * desc.Sk * desc.D
+    _expect(q, nq, dt, "q")
+    _expect(k, nk, dt, "k")
+    _expect(v, nk, dt, "v")
+    for name, t in qlike:
+        _expect(t, nq, dt, name)
+    for name, t in klike:
+        _expect(t, nk, dt, name)
+    for name, t in rowf:
+        _expect(t, desc.B * desc.H * desc.Sq, torch.float32, name)
+    for name, t in accs:
+        _expect(t, nq, torch.float32, name)
+    _expect(seg_q, desc.B * desc.Sq, torch.int32, "seg_q")
+    _expect(seg_k, desc.B * desc.Sk, torch.int32, "seg_k")
+    if table is not None and table.numel() * table.element_size() < lwm_attn_block_table_bytes(desc):
+        raise ValueError("lwm_attn: table buffer smaller than lwm_attn_block_table_bytes(desc)")
+
+
 def make_desc(B, H, Sq, Sk, D, dtype, *, scale=None, causal=True, q_offset=0, k_offset=0,
               block_q=TABLE_BLOCK, block_k=TABLE_BLOCK) -> Desc:
     return Desc(B, H, Sq, Sk, D, int(q_offset), int(k_offset),
@@ -167,6 +211,8 @@ def lwm_attn_build_block_table(desc: Desc, seg_q, seg_k, table=None, stream=None
 
 def lwm_attn_fwd(desc: Desc, mode: int, q, k, v, seg_q, seg_k, table, o=None, lse=None, m=None,
                  l=None, acc=None, stream=None):
+    _expect_attention(desc, q, k, v, seg_q, seg_k, table, qlike=(("o", o),),
+                      rowf=(("lse", lse), ("m", m), ("l", l)), accs=(("acc", acc),))
     rc = load_library().lwm_attn_fwd(ctypes.byref(desc), int(mode), _ptr(q), _ptr(k), _ptr(v),
                                      _ptr(seg_q), _ptr(seg_k), _ptr(table), _ptr(o), _ptr(lse),
                                      _ptr(m), _ptr(l), _ptr(acc), _stream(stream))
@@ -187,6 +233,7 @@ def lwm_attn_decode_workspace_bytes(desc: Desc) -> int:
 
 
 def lwm_attn_decode(desc: Desc, q, k, v, seg_q, seg_k, table, o, lse, workspace, stream=None):
+    _expect_attention(desc, q, k, v, seg_q, seg_k, table, qlike=(("o", o),), rowf=(("lse", lse),))
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = load_library().lwm_attn_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
                                         _ptr(seg_q), _ptr(seg_k), _ptr(table), _ptr(o), _ptr(lse),
@@ -242,8 +289,15 @@ def lwm_attn_bwd_workspace_bytes(desc: Desc) -> int:
     return int(load_library().lwm_attn_bwd_workspace_bytes(ctypes.byref(desc)))
 
 
+def _expect_bwd(desc, q, k, v, o, do, lse, seg_q, seg_k, table, dq, dk, dv):
+    _expect_attention(desc, q, k, v, seg_q, seg_k, table,
+                      qlike=(("o", o), ("dO", do), ("dQ", dq)), klike=(("dK", dk), ("dV", dv)),
+                      rowf=(("lse", lse),))
+
+
 def lwm_attn_bwd(desc: Desc, q, k, v, o, do, lse, seg_q, seg_k, table, dq, dk, dv, workspace,
                  stream=None):
+    _expect_bwd(desc, q, k, v, o, do, lse, seg_q, seg_k, table, dq, dk, dv)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = load_library().lwm_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                      _ptr(do), _ptr(lse), _ptr(seg_q), _ptr(seg_k), _ptr(table),
@@ -254,6 +308,7 @@ def lwm_attn_bwd(desc: Desc, q, k, v, o, do, lse, seg_q, seg_k, table, dq, dk, d
 
 def lwm_attn_bwd_phase(desc: Desc, phase: int, q, k, v, o, do, lse, seg_q, seg_k, table, dq, dk,
                        dv, workspace, stream=None):
+    _expect_bwd(desc, q, k, v, o, do, lse, seg_q, seg_k, table, dq, dk, dv)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = load_library().lwm_attn_bwd_phase(ctypes.byref(desc), int(phase), _ptr(q), _ptr(k),
                                            _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(seg_q),

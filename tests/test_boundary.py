@@ -264,3 +264,47 @@ def test_header_is_plain_c(tmp_path):
     r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
                         "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_python_wrappers_check_buffer_sizes():
+    """The binding raises before any pointer reaches the library when a buffer does not match
+    the desc: a wrong element count or dtype, or a table built for a smaller problem (CPU
+    tensors: the size check comes before the device check)."""
+    torch = pytest.importorskip("torch")
+    d = desc(B=1, H=2, Sq=100, Sk=120)
+    bf = torch.bfloat16
+    q = torch.zeros((1, 2, 100, 128), dtype=bf)
+    k = torch.zeros((1, 2, 120, 128), dtype=bf)
+    sq = torch.zeros((1, 100), dtype=torch.int32)
+    sk = torch.zeros((1, 120), dtype=torch.int32)
+    tab = torch.zeros(lwm.lwm_attn_block_table_bytes(d), dtype=torch.uint8)
+    o = torch.zeros_like(q)
+    lse = torch.zeros((1, 2, 100), dtype=torch.float32)
+    ok = dict(q=q, k=k, v=k, seg_q=sq, seg_k=sk, table=tab, o=o, lse=lse)
+
+    def fwd(**kw):
+        a = {**ok, **kw}
+        lwm.lwm_attn_fwd(d, lwm.LWM_OUT_FINAL, a["q"], a["k"], a["v"], a["seg_q"], a["seg_k"],
+                         a["table"], o=a["o"], lse=a["lse"])
+
+    with pytest.raises(ValueError, match="tensors must live on the GPU"):
+        fwd()                                   # every size right: only the device check fails
+    with pytest.raises(ValueError, match="k has"):
+        fwd(k=torch.zeros((1, 2, 100, 128), dtype=bf))
+    with pytest.raises(ValueError, match="dtype"):
+        fwd(v=k.float())
+    with pytest.raises(ValueError, match="o has"):
+        fwd(o=torch.zeros((1, 2, 99, 128), dtype=bf))
+    with pytest.raises(ValueError, match="lse has"):
+        fwd(lse=torch.zeros((1, 2, 128), dtype=torch.float32))
+    with pytest.raises(ValueError, match="seg_k"):
+        fwd(seg_k=torch.zeros((1, 100), dtype=torch.int32))
+    with pytest.raises(ValueError, match="table"):
+        fwd(table=tab[: tab.numel() - 256])
+    dq, dk = torch.zeros_like(q), torch.zeros_like(k)
+    with pytest.raises(ValueError, match="dV has"):
+        lwm.lwm_attn_bwd(d, q, k, k, o, o, lse, sq, sk, tab, dq, dk, torch.zeros_like(q), None)
+    with pytest.raises(ValueError, match="dO has"):
+        lwm.lwm_attn_bwd_phase(d, lwm.LWM_BWD_DQ, q, k, k, o, k, lse, sq, sk, tab, dq, dk, dk, None)
+    with pytest.raises(ValueError, match="lse has"):
+        lwm.lwm_attn_decode(d, q, k, k, sq, sk, tab, o, lse[:, :1], None)
