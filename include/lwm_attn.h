@@ -23,8 +23,9 @@
  *     accumulator is float32 [B,H,Sq,D].  Segment ids are int32 [B,Sq] / [B,Sk], shared by
  *     all heads.  A negative segment id marks padding: it sees nothing and nothing sees it.
  *   - Every pointer is a device pointer owned by the caller; the library never allocates,
- *     frees or synchronises, and keeps no mutable global state.  `stream` is a hipStream_t
- *     (NULL = the null stream); every call only enqueues work on it and returns.
+ *     frees or synchronises.  Its only mutable global state is the static device buffer of
+ *     lwm_attn_decode_noalloc (one per GPU).  `stream` is a hipStream_t (NULL = the null
+ *     stream); every call only enqueues work on it and returns.
  *   - Device pointers must be 16-byte aligned.  All arguments are validated on the host
  *     before anything is enqueued; on error nothing is enqueued.
  *   - Return value: LWM_OK (0) or a negative LWM_ERR_* code; lwm_attn_status_string()
@@ -147,6 +148,24 @@ size_t lwm_attn_decode_workspace_bytes(const lwm_attn_desc* desc);
 int lwm_attn_decode(const lwm_attn_desc* desc, const void* q, const void* k, const void* v,
                     const int32_t* seg_q, const int32_t* seg_k, const void* table, void* o,
                     float* lse, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * lwm_attn_decode without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The slice states go to a static device buffer of the library instead,
+ * LWM_DECODE_SCRATCH_BYTES per GPU, one copy on each GPU the library runs on, held until the
+ * process ends; the call itself allocates nothing.  When the default split would need more
+ * than the buffer holds, fewer and longer key slices are used (same result up to the order
+ * of float32 rounding).  A request whose states do not fit even with one slice per query
+ * row, i.e. B*H*Sq*(D+2)*4 bytes beyond the buffer (B*H*Sq above about 129000 rows at
+ * D = 128), returns LWM_ERR_WORKSPACE before anything is enqueued.  All calls on one GPU share
+ * its buffer: calls that overlap on one GPU (two streams or two threads) race and must be
+ * serialised by the caller.  Other arguments, results and errors as lwm_attn_decode.
+ */
+#define LWM_DECODE_SCRATCH_BYTES ((size_t)64 << 20)
+int lwm_attn_decode_noalloc(const lwm_attn_desc* desc, const void* q, const void* k,
+                            const void* v, const int32_t* seg_q, const int32_t* seg_k,
+                            const void* table, void* o, float* lse, void* stream);
 
 /*
  * Backward of the forward above for an upstream gradient dO, recomputing P from the saved

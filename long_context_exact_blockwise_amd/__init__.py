@@ -43,8 +43,9 @@ EXPORTED = (
     "lwm_attn_merge_chunk", "lwm_attn_bwd_workspace_bytes", "lwm_attn_bwd",
     "lwm_attn_bwd_phase", "lwm_attn_status_string", "lwm_attn_version",
     "lwm_attn_decode_workspace_bytes", "lwm_attn_decode", "lwm_attn_rope",
-    "lwm_attn_packed_loss_workspace_bytes", "lwm_attn_packed_loss",
+    "lwm_attn_packed_loss_workspace_bytes", "lwm_attn_packed_loss", "lwm_attn_decode_noalloc",
 )
+DECODE_SCRATCH_BYTES = 64 << 20  # LWM_DECODE_SCRATCH_BYTES
 LWM_BWD_DELTA, LWM_BWD_DQ, LWM_BWD_DKV = 0, 1, 2
 
 
@@ -87,6 +88,7 @@ def load_library(path: str = LIB_PATH):
         "lwm_attn_bwd_phase": (ctypes.c_int, [DP, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "lwm_attn_decode_workspace_bytes": (SZ, [DP]),
         "lwm_attn_decode": (ctypes.c_int, [DP, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "lwm_attn_decode_noalloc": (ctypes.c_int, [DP, P, P, P, P, P, P, P, P, P]),
         "lwm_attn_rope": (ctypes.c_int, [I32, I32, I32, I32, I32, I64, ctypes.c_double, I32, P, P, P]),
         "lwm_attn_packed_loss_workspace_bytes": (SZ, [I32, I32, I32, I32]),
         "lwm_attn_packed_loss": (ctypes.c_int, [I32, I32, I32, I32, I32, P, P, P, ctypes.c_float, P, P,
@@ -239,6 +241,16 @@ def lwm_attn_decode(desc: Desc, q, k, v, seg_q, seg_k, table, o, lse, workspace,
                                         _ptr(seg_q), _ptr(seg_k), _ptr(table), _ptr(o), _ptr(lse),
                                         _ptr(workspace), ws_bytes, _stream(stream))
     _check("lwm_attn_decode", rc)
+
+
+def lwm_attn_decode_noalloc(desc: Desc, q, k, v, seg_q, seg_k, table, o, lse, stream=None):
+    """lwm_attn_decode with the slice states in the library's static device buffer: the call
+    allocates nothing.  Calls that overlap on one GPU race on that buffer."""
+    _expect_attention(desc, q, k, v, seg_q, seg_k, table, qlike=(("o", o),), rowf=(("lse", lse),))
+    rc = load_library().lwm_attn_decode_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                                _ptr(seg_q), _ptr(seg_k), _ptr(table), _ptr(o),
+                                                _ptr(lse), _stream(stream))
+    _check("lwm_attn_decode_noalloc", rc)
 
 
 def lwm_attn_rope(x, out, pos_offset: int, theta: float, inverse: bool = False, stream=None):

@@ -21,7 +21,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "table.hip", "attn_f32.hip", "attn_bf16.hip", "merge.hip", "rope.hip",
-           "packed_loss.hip"]
+           "packed_loss.hip", "decode_noalloc.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result",

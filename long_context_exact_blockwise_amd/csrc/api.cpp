@@ -126,8 +126,27 @@ int lwm_attn_decode(const lwm_attn_desc* d, const void* q, const void* k, const 
   const void* ptrs[] = {q, k, v, seg_q, seg_k, table, o, lse, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return LWM_ERR_ALIGNMENT;
-  return hip_status(lwm::launch_decode_bf16(*d, q, k, v, seg_q, seg_k, table, o, lse, workspace,
+  return hip_status(lwm::launch_decode_bf16(*d, lwm::decode_layout(*d), q, k, v, seg_q, seg_k,
+                                            table, o, lse, workspace,
                                             static_cast<hipStream_t>(stream)));
+}
+
+int lwm_attn_decode_noalloc(const lwm_attn_desc* d, const void* q, const void* k, const void* v,
+                            const int32_t* seg_q, const int32_t* seg_k, const void* table,
+                            void* o, float* lse, void* stream) {
+  int rc = check_attention_desc(d);
+  if (rc) return rc;
+  if (d->dtype != LWM_BF16) return LWM_ERR_UNSUPPORTED;
+  if (d->Sq == 0) return LWM_OK;
+  if (!q || !seg_q || !table || !o || !lse) return LWM_ERR_INVALID_ARG;
+  if (d->Sk > 0 && (!k || !v || !seg_k)) return LWM_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, seg_q, seg_k, table, o, lse};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return LWM_ERR_ALIGNMENT;
+  lwm::DecodeLayout L;
+  if (!lwm::decode_layout_capped(*d, lwm::kDecodeScratchBytes, &L)) return LWM_ERR_WORKSPACE;
+  return hip_status(lwm::launch_decode_bf16_noalloc(*d, L, q, k, v, seg_q, seg_k, table, o, lse,
+                                                    static_cast<hipStream_t>(stream)));
 }
 
 int lwm_attn_merge_chunk(int64_t rows, int32_t D, float* m, float* l, float* acc, const float* mc,

@@ -1068,12 +1068,12 @@ hipError_t launch_fwd_bf16(const lwm_attn_desc& d, int mode, const void* q, cons
 }
 
 // Split-KV decode: the forward in PARTIAL form with grid (query tiles x heads x batch,
-// slices), then the combine.  Workspace layout: decode_layout.
-hipError_t launch_decode_bf16(const lwm_attn_desc& d, const void* q, const void* k, const void* v,
-                              const int32_t* seg_q, const int32_t* seg_k, const void* table,
-                              void* o, float* lse, void* workspace, hipStream_t stream) {
+// slices), then the combine.  Workspace layout: L.
+hipError_t launch_decode_bf16(const lwm_attn_desc& d, const DecodeLayout& L, const void* q,
+                              const void* k, const void* v, const int32_t* seg_q,
+                              const int32_t* seg_k, const void* table, void* o, float* lse,
+                              void* workspace, hipStream_t stream) {
   const TableView t = table_view(d, table);
-  const DecodeLayout L = decode_layout(d);
   char* ws = static_cast<char*>(workspace);
   float* m = reinterpret_cast<float*>(ws + L.m_off);
   float* l = reinterpret_cast<float*>(ws + L.l_off);

@@ -73,6 +73,19 @@ struct DecodeLayout {
   size_t m_off, l_off, acc_off, total;
 };
 
+inline DecodeLayout decode_layout_for(const lwm_attn_desc& d, int64_t split_tiles) {
+  const int64_t nkt = (int64_t(d.Sk) + 63) / 64;
+  DecodeLayout L;
+  L.split_tiles = split_tiles;
+  L.nsplit = nkt > 0 ? (nkt + split_tiles - 1) / split_tiles : 1;
+  const size_t rows = size_t(d.B) * d.H * d.Sq;
+  L.m_off = 0;
+  L.l_off = align256(size_t(L.nsplit) * rows * sizeof(float));
+  L.acc_off = L.l_off + align256(size_t(L.nsplit) * rows * sizeof(float));
+  L.total = L.acc_off + align256(size_t(L.nsplit) * rows * d.D * sizeof(float));
+  return L;
+}
+
 inline DecodeLayout decode_layout(const lwm_attn_desc& d) {
   const int64_t nkt = (int64_t(d.Sk) + 63) / 64;
   const int64_t base = (int64_t(d.Sq) + 127) / 128 * d.H * d.B;
@@ -80,15 +93,25 @@ inline DecodeLayout decode_layout(const lwm_attn_desc& d) {
   int64_t st = (nkt + want - 1) / want;
   if (st < kDecodeMinTiles) st = kDecodeMinTiles;
   if (st < (nkt + 65534) / 65535) st = (nkt + 65534) / 65535;
-  DecodeLayout L;
-  L.split_tiles = st;
-  L.nsplit = nkt > 0 ? (nkt + st - 1) / st : 1;
-  const size_t rows = size_t(d.B) * d.H * d.Sq;
-  L.m_off = 0;
-  L.l_off = align256(size_t(L.nsplit) * rows * sizeof(float));
-  L.acc_off = L.l_off + align256(size_t(L.nsplit) * rows * sizeof(float));
-  L.total = L.acc_off + align256(size_t(L.nsplit) * rows * d.D * sizeof(float));
-  return L;
+  return decode_layout_for(d, st);
+}
+
+// The same split with at most max_bytes of slice states: fewer, longer slices when the
+// default split needs more.  False when even one slice per row does not fit.
+inline bool decode_layout_capped(const lwm_attn_desc& d, size_t max_bytes, DecodeLayout* out) {
+  DecodeLayout L = decode_layout(d);
+  if (L.total > max_bytes) {
+    const size_t per_slice = size_t(d.B) * d.H * d.Sq * (size_t(d.D) + 2) * sizeof(float);
+    if (per_slice == 0 || max_bytes < 3 * 256 + per_slice) return false;
+    const int64_t max_slices = int64_t((max_bytes - 3 * 256) / per_slice);
+    const int64_t nkt = (int64_t(d.Sk) + 63) / 64;
+    int64_t st = (nkt + max_slices - 1) / max_slices;
+    if (st < L.split_tiles) st = L.split_tiles;
+    L = decode_layout_for(d, st);
+    if (L.total > max_bytes) return false;
+  }
+  *out = L;
+  return true;
 }
 
 // Packed-loss workspace: per-sample loss-token counters int32 [B][nseg], the sample count
@@ -131,9 +154,20 @@ hipError_t launch_fwd_bf16(const lwm_attn_desc& d, int mode, const void* q, cons
                            const void* table, void* o, float* lse, float* m, float* l,
                            float* acc, hipStream_t stream);
 
-hipError_t launch_decode_bf16(const lwm_attn_desc& d, const void* q, const void* k, const void* v,
-                              const int32_t* seg_q, const int32_t* seg_k, const void* table,
-                              void* o, float* lse, void* workspace, hipStream_t stream);
+// Slice states in `workspace` laid out as L (decode_layout or decode_layout_capped).
+hipError_t launch_decode_bf16(const lwm_attn_desc& d, const DecodeLayout& L, const void* q,
+                              const void* k, const void* v, const int32_t* seg_q,
+                              const int32_t* seg_k, const void* table, void* o, float* lse,
+                              void* workspace, hipStream_t stream);
+
+// Decode with its slice states in the library's own static device buffer of
+// kDecodeScratchBytes per device (decode_noalloc.hip); LWM_ERR_WORKSPACE-worthy sizes are
+// rejected by the caller with decode_layout_capped first.
+constexpr size_t kDecodeScratchBytes = size_t(64) << 20;
+hipError_t launch_decode_bf16_noalloc(const lwm_attn_desc& d, const DecodeLayout& L, const void* q,
+                                      const void* k, const void* v, const int32_t* seg_q,
+                                      const int32_t* seg_k, const void* table, void* o,
+                                      float* lse, hipStream_t stream);
 
 hipError_t launch_bwd_bf16(const lwm_attn_desc& d, int phase, const void* q, const void* k, const void* v,
                            const void* o, const void* dO, const float* lse,

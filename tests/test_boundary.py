@@ -199,6 +199,29 @@ def test_decode_rejects_bad_arguments(lib):
                 ws=None, ws_bytes=0) == OK
 
 
+def test_decode_noalloc_rejects_bad_arguments_and_oversize(lib):
+    f = lib.lwm_attn_decode_noalloc
+
+    def call(d, **kw):
+        names = ("q", "k", "v", "sq", "sk", "t", "o", "lse")
+        return f(ctypes.byref(d), *[kw.get(n, FAKE) for n in names], None)
+
+    assert lwm.DECODE_SCRATCH_BYTES == 64 << 20
+    assert call(desc(D=64, dtype=lwm.LWM_F32)) == UNSUP
+    assert call(desc(block_k=32)) == UNSUP
+    assert call(desc(scale=0.0)) == INVALID
+    assert call(desc(), o=None) == INVALID
+    assert call(desc(), lse=None) == INVALID
+    assert call(desc(), v=FAKE + 8) == ALIGN
+    # one slice state per query row: B*H*Sq*(D+2)*4 bytes (plus three 256-byte alignments)
+    # must fit the 64 MiB buffer; 129000 rows fit, 129100 do not; rejected on the host
+    fits = (lwm.DECODE_SCRATCH_BYTES - 3 * 256) // (130 * 4)
+    assert call(desc(H=1, Sq=fits + 1, Sk=4096)) == WS
+    assert call(desc(B=2, H=32, Sq=4096, Sk=1 << 20)) == WS
+    assert call(desc(Sq=0), q=None, k=None, v=None, sq=None, sk=None, t=None, o=None,
+                lse=None) == OK
+
+
 def test_rope_rejects_bad_arguments(lib):
     f = lib.lwm_attn_rope
 
@@ -308,3 +331,5 @@ def test_python_wrappers_check_buffer_sizes():
         lwm.lwm_attn_bwd_phase(d, lwm.LWM_BWD_DQ, q, k, k, o, k, lse, sq, sk, tab, dq, dk, dk, None)
     with pytest.raises(ValueError, match="lse has"):
         lwm.lwm_attn_decode(d, q, k, k, sq, sk, tab, o, lse[:, :1], None)
+    with pytest.raises(ValueError, match="o has"):
+        lwm.lwm_attn_decode_noalloc(d, q, k, k, sq, sk, tab, k, lse)
