@@ -21,6 +21,7 @@ import json
 import math
 import os
 import platform
+import re
 import sys
 import time
 
@@ -249,16 +250,20 @@ def rocminfo_peak():
         out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
     except Exception as e:  # pragma: no cover - rocminfo missing
         return {"error": f"rocminfo not run: {e}"}
-    agent, found = {}, None
-    for line in out.splitlines():
-        t = line.strip()
-        if t.startswith("Name:") and "gfx950" in t:
-            found = agent = {"name": t.split(":", 1)[1].strip()}
-        elif found is not None and t.startswith("Compute Unit:") and "cus" not in agent:
-            agent["cus"] = int(t.split(":", 1)[1])
-        elif found is not None and t.startswith("Max Clock Freq. (MHz):") and "mhz" not in agent:
-            agent["mhz"] = int(t.split(":", 1)[1].split()[0])
-    if not found or "cus" not in agent or "mhz" not in agent:
+    # one section per agent ("Agent N" ... ), each with its own Name / clock / CU lines; the
+    # ISA entries nested in a GPU agent carry longer names (amdgcn-amd-amdhsa--gfx950...)
+    agent = None
+    for sec in re.split(r"\n(?=Agent \d+)", out):
+        f = {}
+        for line in sec.splitlines():
+            k, _, v = line.strip().partition(":")
+            if k in ("Name", "Compute Unit", "Max Clock Freq. (MHz)") and k not in f:
+                f[k] = v.strip()
+        if f.get("Name") == "gfx950" and "Compute Unit" in f and "Max Clock Freq. (MHz)" in f:
+            agent = {"name": f["Name"], "cus": int(f["Compute Unit"]),
+                     "mhz": int(f["Max Clock Freq. (MHz)"].split()[0])}
+            break
+    if agent is None:
         return {"error": "no gfx950 agent with compute units and clock in rocminfo output"}
     agent["flop_per_clk_per_cu"] = 4096
     agent["peak_tflops"] = agent["cus"] * agent["mhz"] * 1e6 * 4096 / 1e12
