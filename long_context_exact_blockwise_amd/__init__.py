@@ -20,13 +20,18 @@ Convenience layers on top of those calls:
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
 from typing import List, Optional, Sequence, Tuple
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "liblwm_attn.so")
+# LWM_ATTN_LIBRARY names another build of the same library (the host-sanitizer build of the
+# boundary tests); by default the in-tree build is loaded
+LIB_PATH = os.environ.get("LWM_ATTN_LIBRARY") or os.path.join(_PKG, "liblwm_attn.so")
+# the race-canary build of the bf16 kernels (see build.py)
+CANARY_LIB_PATH = os.path.join(_PKG, "liblwm_attn_canary.so")
 
 LWM_BF16, LWM_F32 = 0, 1
 LWM_OUT_FINAL, LWM_OUT_PARTIAL = 0, 1
@@ -66,13 +71,35 @@ class Desc(ctypes.Structure):
 
 
 _lib = None
+_opened = {}
 
 
 def load_library(path: str = LIB_PATH):
-    """Load the shared library (once) and declare its signatures."""
+    """Load the shared library (once) and declare its signatures; every wrapper below calls
+    the library loaded first (or the one active_library() selects)."""
     global _lib
     if _lib is not None:
         return _lib
+    _lib = _open_library(path)
+    return _lib
+
+
+@contextlib.contextmanager
+def active_library(path: str):
+    """Run the wrappers against another build of the library (the race-canary build) inside
+    a `with` block."""
+    global _lib
+    prev = _lib
+    _lib = _open_library(path)
+    try:
+        yield _lib
+    finally:
+        _lib = prev
+
+
+def _open_library(path: str):
+    if path in _opened:
+        return _opened[path]
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built: run `python -m long_context_exact_blockwise_amd.build`")
     lib = ctypes.CDLL(path)
@@ -100,7 +127,7 @@ def load_library(path: str = LIB_PATH):
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    _lib = lib
+    _opened[path] = lib
     return lib
 
 

@@ -35,9 +35,16 @@ COMMON_FLAGS = [
 SOURCE_FLAGS = {"attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS, *SOURCE_FLAGS.get(src, [])]
+# The race-canary build: the bf16 attention kernels with a wait and a workgroup barrier after
+# every phase of a tile step (LWM_RACE_CANARY), linked into a library of its own that the GPU
+# tests compare bit for bit with the normal one.
+CANARY_LIB = os.path.join(PKG, "liblwm_attn_canary.so")
+CANARY_SOURCES = {"attn_bf16.hip": ["-DLWM_RACE_CANARY"]}
+
+
+def _compile(src: str, extra=(), suffix: str = "") -> str:
+    obj = os.path.join(BUILD, os.path.basename(src) + suffix + ".o")
+    cmd = [HIPCC, *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), *extra]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
@@ -47,19 +54,31 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source, link the shared library and its race-canary twin; returns the
+    library's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = [(src, (), "") for src in SOURCES]
+    jobs += [(src, tuple(flags), ".canary") for src, flags in CANARY_SOURCES.items()]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    normal = objs[:len(SOURCES)]
+    canary = [o for o in normal]
+    for (src, _, _), o in zip(jobs[len(SOURCES):], objs[len(SOURCES):]):
+        canary[SOURCES.index(src)] = o
+    _link(normal, LIB)
+    _link(canary, CANARY_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CANARY_LIB}")
     return LIB
 
 

@@ -264,6 +264,19 @@ __device__ __forceinline__ void sdp_chain(f32x16& sacc, f32x16& pacc, const uint
 // Wait until this wave's outstanding vector-memory loads (including loads into LDS) are done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Race canary.  Built with LWM_RACE_CANARY, every phase of a tile step that reads LDS, or
+// issues loads into it, is followed by a wait for this wave's loads and a workgroup barrier,
+// so no wave can run ahead of another into a buffer it shares.  A schedule whose single
+// barrier per tile leaves a race gives results that differ from this build's; the GPU tests
+// compare the two bit for bit.  In the normal build the calls compile to nothing.
+__device__ __forceinline__ void canary_sync() {
+#ifdef LWM_RACE_CANARY
+  wait_vmem();
+  __syncthreads();
+#endif
+}
+
+
 // ---------------------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------------------
@@ -389,6 +402,10 @@ __device__ __forceinline__ void fwd_bf16_body(AttnParams p, TableView t, int mod
     const bool more = kn <= c1;
     if (!wave_live) {
       if (more) issue(kn, kn_lds, vn_lds, sn_lds);
+      // as many canary barriers as the live path below
+      canary_sync();
+      canary_sync();
+      canary_sync();
       advance();
       return;
     }
@@ -400,6 +417,7 @@ __device__ __forceinline__ void fwd_bf16_body(AttnParams p, TableView t, int mod
     } else {
       scores(sacc, kb_lds, NoDma{});
     }
+    canary_sync();
 
     if (st == LWM_TILE_PARTIAL) {
       // branch-free visibility; rows past Sq carry sq = -1 and see nothing
@@ -443,6 +461,7 @@ __device__ __forceinline__ void fwd_bf16_body(AttnParams p, TableView t, int mod
         }
         pb[2 * sub + a] = to_bf16x8(pv);
       }
+    canary_sync();
     l_run = l_run * alpha + ((ps4[0] + ps4[1]) + (ps4[2] + ps4[3]));
     if (__ballot(upd) != 0) {
 #pragma unroll
@@ -465,6 +484,7 @@ __device__ __forceinline__ void fwd_bf16_body(AttnParams p, TableView t, int mod
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 2);
+    canary_sync();
     advance();
   };
 
@@ -676,6 +696,7 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
   const int qrow = qt * BQ + wave * 32 + col;
   const bool qlive = qrow < p.Sq;
   const int64_t r64 = bh * p.Sq + qrow;
+  int64_t rbase = bh * p.Sq + qt * BQ + wave * 32;  // row of the wave's lane 0 (uniform)
   bf16x8 qreg[D / 16], greg[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
@@ -780,12 +801,14 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
       // keep the two 32-key halves' scores apart: overlapping them would need a second set
       // of score registers, which does not fit beside two waves per SIMD
       __builtin_amdgcn_sched_barrier(0);
+      canary_sync();
     }
 #pragma unroll
     for (int ks = 2; ks < BK / 16; ++ks)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
         dqacc[db] = mfma32(lds_load_tr8(kb_lds, 16 * ks, 32 * db, lane), dsb[ks], dqacc[db]);
+    canary_sync();
     kt = kn;
   };
 
@@ -803,7 +826,10 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
     }
   }
   if (!qlive) return;
-  uint16_t* out = dQ + r64 * D;
+  // the output row formed again from scalars, so no 64-bit per-lane offset stays live across
+  // the tile loop (it was spilled to scratch at two waves per SIMD)
+  asm volatile("" : "+s"(rbase));
+  uint16_t* out = dQ + (rbase + col) * D;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -948,6 +974,7 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
     else
       sdp_chain(sacc[0], pacc[0], qb_lds, gb_lds, kperm(col), hf, kreg, vreg, NoDma{});
     sdp_chain(sacc[1], pacc[1], qb_lds, gb_lds, 32 + kperm(col), hf, kreg, vreg, NoDma{});
+    canary_sync();
     if (st == LWM_TILE_PARTIAL) {
       // hidden scores become -inf, so their probabilities come out as exactly 0; keys past Sk
       // carry sk = -2 and see no row
@@ -996,6 +1023,7 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
       pb[ks] = to_bf16x8(pv);
       dsb[ks] = to_bf16x8(ds);
     }
+    canary_sync();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int m = 0; m < 32; ++m) {
@@ -1007,6 +1035,7 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
       if (m + kAhead < 32) opread(m + kAhead);
       __builtin_amdgcn_sched_barrier(0);
     }
+    canary_sync();
     st_c = uniform(st_n);
     qn_c = (qn + 1 <= w1 && uniform(s_after) == LWM_TILE_SKIP) ? next_live_lds(stat_lds, w0, qn + 2, w1)
                                                                 : qn + 1;
