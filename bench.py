@@ -579,7 +579,37 @@ def main() -> int:
         parts["rope_qk"] = {"ms": ms_rope, "algo_bytes": rope_bytes, "theta": 1e7,
                             "gbs": rope_bytes / (ms_rope * 1e-3) / 1e9,
                             "frac_hbm_peak": rope_bytes / (ms_rope * 1e-3) / 1e9 / PEAK_HBM_GBS}
-        del qr, kr
+        # a training step with RoPE (theta = 10M): Q or K turned inside the attention kernels'
+        # loads (K before the forward, Q and K before the backward: three streaming passes)
+        # against turning Q and K first and dQ, dK back after (six passes)
+        th = 1e7
+        qr2, kr2 = torch.empty_like(x["q"]), torch.empty_like(x["k"])
+
+        def rope_step_at_load():
+            lwm.lwm_attn_rope(x["k"], kr, 0, th)
+            lwm.lwm_attn_fwd_rope(desc, lwm.LWM_OUT_FINAL, th, x["q"], kr, x["v"], sq, sk, table, o=o, lse=lse)
+            lwm.lwm_attn_rope(x["q"], qr2, 0, th)
+            lwm.lwm_attn_rope(x["k"], kr2, 0, th)
+            lwm.lwm_attn_bwd_rope(desc, th, x["q"], qr2, x["k"], kr2, x["v"], o, x["do"], lse, sq, sk,
+                                  table, dq, dk, dv, ws)
+
+        def rope_step_first():
+            lwm.lwm_attn_rope(x["q"], qr, 0, th)
+            lwm.lwm_attn_rope(x["k"], kr, 0, th)
+            lwm.lwm_attn_fwd(desc, lwm.LWM_OUT_FINAL, qr, kr, x["v"], sq, sk, table, o=o, lse=lse)
+            lwm.lwm_attn_rope(x["q"], qr2, 0, th)
+            lwm.lwm_attn_rope(x["k"], kr2, 0, th)
+            lwm.lwm_attn_bwd(desc, qr2, kr2, x["v"], o, x["do"], lse, sq, sk, table, dq, dk, dv, ws)
+            lwm.lwm_attn_rope(dq, dq, 0, th, inverse=True)
+            lwm.lwm_attn_rope(dk, dk, 0, th, inverse=True)
+
+        parts["rope_step_at_load"] = {"ms": time_events(rope_step_at_load, reps), "theta": th,
+                                      "note": "fwd + bwd with RoPE inside the kernels' loads, 3 RoPE passes"}
+        parts["rope_step_turn_first"] = {"ms": time_events(rope_step_first, reps), "theta": th,
+                                         "note": "fwd + bwd on Q, K turned first, dQ, dK turned back, 6 RoPE passes"}
+        print(f"[bench] RoPE step: at load {parts['rope_step_at_load']['ms']:.3f} ms, turned first "
+              f"{parts['rope_step_turn_first']['ms']:.3f} ms", file=sys.stderr, flush=True)
+        del qr, kr, qr2, kr2
         dom = max(("fwd", "bwd_dq", "bwd_dkv"), key=lambda k: parts[k]["ms"])
         traffic = None
         if os.path.exists(TRAFFIC_FILE):

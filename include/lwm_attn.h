@@ -221,6 +221,36 @@ int lwm_attn_rope(int32_t B, int32_t H, int32_t S, int32_t D, int32_t dtype, int
                   double theta, int32_t inverse, const void* x, void* out, void* stream);
 
 /*
+ * Attention with RoPE applied inside the tile loop's register load, for the step before
+ * Q K^T of every layer of the LWM model (deep dive, section "Stage I：长上下文语言模型" and
+ * Tables 11 and 13: RoPE with a base theta grown from 1M to 50M as the context grows).  The
+ * operand a kernel keeps in registers arrives unrotated and is turned at load by global
+ * position; the operand it streams arrives turned already, from lwm_attn_rope with the same
+ * theta and positions (q_offset / k_offset of desc).  The turn at load computes exactly what
+ * lwm_attn_rope computes for the same element, so the result equals lwm_attn_fwd /
+ * lwm_attn_bwd on turned inputs.
+ *   lwm_attn_fwd_rope: q unrotated, k_rot = lwm_attn_rope(k, k_offset, theta); otherwise as
+ *     lwm_attn_fwd (both modes).
+ *   lwm_attn_bwd_rope: q and k unrotated, q_rot and k_rot turned; o and lse from the forward.
+ *     dq and dk are the gradients of the unrotated q and k (the gradients of the turned ones,
+ *     turned back in float32 before rounding), dv as lwm_attn_bwd.  Workspace as lwm_attn_bwd.
+ * Supported: dtype LWM_BF16 with D = 128 (else LWM_ERR_UNSUPPORTED); theta > 1 and finite
+ * (else LWM_ERR_INVALID_ARG); q_offset + Sq and k_offset + Sk at most 2^32 (else
+ * LWM_ERR_SHAPE).  Over a training step this replaces six streaming RoPE passes (Q and K
+ * before the forward and again before the backward, dQ and dK after it) by three (K before
+ * the forward, Q and K before the backward).
+ */
+int lwm_attn_fwd_rope(const lwm_attn_desc* desc, int32_t mode, double theta, const void* q,
+                      const void* k_rot, const void* v, const int32_t* seg_q,
+                      const int32_t* seg_k, const void* table, void* o, float* lse, float* m,
+                      float* l, float* acc, void* stream);
+int lwm_attn_bwd_rope(const lwm_attn_desc* desc, double theta, const void* q, const void* q_rot,
+                      const void* k, const void* k_rot, const void* v, const void* o,
+                      const void* dO, const float* lse, const int32_t* seg_q,
+                      const int32_t* seg_k, const void* table, void* dq, void* dk, void* dv,
+                      void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Packed-sequence loss reweighting, the step after attention in the packed path: the LWM
  * pages reweight the loss of a packed sequence so that it equals training its samples
  * unpacked with padding, so that samples with many tokens (long videos) do not outweigh

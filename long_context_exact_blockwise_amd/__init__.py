@@ -49,6 +49,7 @@ EXPORTED = (
     "lwm_attn_bwd_phase", "lwm_attn_status_string", "lwm_attn_version",
     "lwm_attn_decode_workspace_bytes", "lwm_attn_decode", "lwm_attn_rope",
     "lwm_attn_packed_loss_workspace_bytes", "lwm_attn_packed_loss", "lwm_attn_decode_noalloc",
+    "lwm_attn_fwd_rope", "lwm_attn_bwd_rope",
 )
 DECODE_SCRATCH_BYTES = 64 << 20  # LWM_DECODE_SCRATCH_BYTES
 LWM_BWD_DELTA, LWM_BWD_DQ, LWM_BWD_DKV = 0, 1, 2
@@ -116,6 +117,10 @@ def _open_library(path: str):
         "lwm_attn_decode_workspace_bytes": (SZ, [DP]),
         "lwm_attn_decode": (ctypes.c_int, [DP, P, P, P, P, P, P, P, P, P, SZ, P]),
         "lwm_attn_decode_noalloc": (ctypes.c_int, [DP, P, P, P, P, P, P, P, P, P]),
+        "lwm_attn_fwd_rope": (ctypes.c_int, [DP, I32, ctypes.c_double, P, P, P, P, P, P, P, P, P, P,
+                                             P, P]),
+        "lwm_attn_bwd_rope": (ctypes.c_int, [DP, ctypes.c_double, P, P, P, P, P, P, P, P, P, P, P,
+                                             P, P, P, P, SZ, P]),
         "lwm_attn_rope": (ctypes.c_int, [I32, I32, I32, I32, I32, I64, ctypes.c_double, I32, P, P, P]),
         "lwm_attn_packed_loss_workspace_bytes": (SZ, [I32, I32, I32, I32]),
         "lwm_attn_packed_loss": (ctypes.c_int, [I32, I32, I32, I32, I32, P, P, P, ctypes.c_float, P, P,
@@ -248,6 +253,18 @@ def lwm_attn_fwd(desc: Desc, mode: int, q, k, v, seg_q, seg_k, table, o=None, ls
     _check("lwm_attn_fwd", rc)
 
 
+def lwm_attn_fwd_rope(desc: Desc, mode: int, theta: float, q, k_rot, v, seg_q, seg_k, table, o=None,
+                      lse=None, m=None, l=None, acc=None, stream=None):
+    """lwm_attn_fwd with q unrotated (turned by RoPE at load) and k_rot turned already."""
+    _expect_attention(desc, q, k_rot, v, seg_q, seg_k, table, qlike=(("o", o),),
+                      rowf=(("lse", lse), ("m", m), ("l", l)), accs=(("acc", acc),))
+    rc = load_library().lwm_attn_fwd_rope(ctypes.byref(desc), int(mode), float(theta), _ptr(q),
+                                          _ptr(k_rot), _ptr(v), _ptr(seg_q), _ptr(seg_k),
+                                          _ptr(table), _ptr(o), _ptr(lse), _ptr(m), _ptr(l),
+                                          _ptr(acc), _stream(stream))
+    _check("lwm_attn_fwd_rope", rc)
+
+
 def lwm_attn_merge_chunk(rows: int, D: int, m, l, acc, mc=None, lc=None, accc=None,
                          finalize: bool = False, out_dtype: int = LWM_BF16, o=None, lse=None,
                          stream=None):
@@ -345,6 +362,21 @@ def lwm_attn_bwd(desc: Desc, q, k, v, o, do, lse, seg_q, seg_k, table, dq, dk, d
     _check("lwm_attn_bwd", rc)
 
 
+def lwm_attn_bwd_rope(desc: Desc, theta: float, q, q_rot, k, k_rot, v, o, do, lse, seg_q, seg_k,
+                      table, dq, dk, dv, workspace, stream=None):
+    """lwm_attn_bwd with RoPE at load: q, k unrotated, q_rot, k_rot turned; dq, dk are the
+    gradients of the unrotated q, k."""
+    _expect_bwd(desc, q, k, v, o, do, lse, seg_q, seg_k, table, dq, dk, dv)
+    _expect_attention(desc, q_rot, k_rot)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load_library().lwm_attn_bwd_rope(ctypes.byref(desc), float(theta), _ptr(q), _ptr(q_rot),
+                                          _ptr(k), _ptr(k_rot), _ptr(v), _ptr(o), _ptr(do),
+                                          _ptr(lse), _ptr(seg_q), _ptr(seg_k), _ptr(table),
+                                          _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes,
+                                          _stream(stream))
+    _check("lwm_attn_bwd_rope", rc)
+
+
 def lwm_attn_bwd_phase(desc: Desc, phase: int, q, k, v, o, do, lse, seg_q, seg_k, table, dq, dk,
                        dv, workspace, stream=None):
     _expect_bwd(desc, q, k, v, o, do, lse, seg_q, seg_k, table, dq, dk, dv)
@@ -382,19 +414,36 @@ def _rotated(q, k, rope_theta, q_offset, k_offset, stream):
     return (rope(q, q_offset, rope_theta, stream=stream), rope(k, k_offset, rope_theta, stream=stream))
 
 
+def _rope_at_load(q, rope_theta) -> bool:
+    """RoPE inside the attention kernels' loads is built for bf16 with head width 128; other
+    dtypes and widths turn Q and K with the standalone kernel first."""
+    import torch
+
+    return rope_theta is not None and q.dtype == torch.bfloat16 and q.shape[-1] == 128
+
+
 def attention_forward(q, k, v, seg_q, seg_k, *, scale=None, causal=True, q_offset=0, k_offset=0,
                       table=None, rope_theta=None, stream=None):
     """(O, LSE, table) for Q [B,H,Sq,D] against K, V [B,H,Sk,D] with segment ids.  With
-    rope_theta, Q and K are first rotated by RoPE at their global positions."""
+    rope_theta, Q and K are turned by RoPE at their global positions: K by the standalone
+    kernel and Q inside the attention kernel's load (bf16, D = 128), or both first."""
     import torch
 
-    q, k = _rotated(q, k, rope_theta, q_offset, k_offset, stream)
+    fused = _rope_at_load(q, rope_theta)
+    if fused:
+        k = rope(k, k_offset, rope_theta, stream=stream)
+    else:
+        q, k = _rotated(q, k, rope_theta, q_offset, k_offset, stream)
     desc = _desc_for(q, k, scale=scale, causal=causal, q_offset=q_offset, k_offset=k_offset)
     if table is None:
         table = lwm_attn_build_block_table(desc, seg_q, seg_k, stream=stream)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    lwm_attn_fwd(desc, LWM_OUT_FINAL, q, k, v, seg_q, seg_k, table, o=o, lse=lse, stream=stream)
+    if fused:
+        lwm_attn_fwd_rope(desc, LWM_OUT_FINAL, rope_theta, q, k, v, seg_q, seg_k, table, o=o, lse=lse,
+                          stream=stream)
+    else:
+        lwm_attn_fwd(desc, LWM_OUT_FINAL, q, k, v, seg_q, seg_k, table, o=o, lse=lse, stream=stream)
     return o, lse, table
 
 
@@ -441,9 +490,22 @@ def attention_partial(q, k, v, seg_q, seg_k, *, scale=None, causal=True, q_offse
 def attention_backward(q, k, v, o, do, lse, seg_q, seg_k, table, *, scale=None, causal=True,
                        q_offset=0, k_offset=0, workspace=None, rope_theta=None, stream=None):
     """(dQ, dK, dV) by LSE recompute.  With rope_theta, q and k are the unrotated inputs of a
-    RoPE forward: they are rotated again, and dQ, dK are rotated back (in place)."""
+    RoPE forward and dQ, dK the gradients of those: for bf16 with D = 128 the kernels turn
+    the operand they hold at load and turn dQ, dK back before rounding (Q and K are also
+    turned once by the standalone kernel, for the operand each kernel streams); otherwise Q
+    and K are turned first and dQ, dK turned back after (in place)."""
     import torch
 
+    if _rope_at_load(q, rope_theta):
+        desc = _desc_for(q, k, scale=scale, causal=causal, q_offset=q_offset, k_offset=k_offset)
+        if workspace is None:
+            workspace = torch.empty(max(lwm_attn_bwd_workspace_bytes(desc), 16), dtype=torch.uint8,
+                                    device=q.device)
+        q_rot, k_rot = _rotated(q, k, rope_theta, q_offset, k_offset, stream)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        lwm_attn_bwd_rope(desc, rope_theta, q, q_rot, k, k_rot, v, o, do, lse, seg_q, seg_k, table,
+                          dq, dk, dv, workspace, stream=stream)
+        return dq, dk, dv
     q, k = _rotated(q, k, rope_theta, q_offset, k_offset, stream)
     desc = _desc_for(q, k, scale=scale, causal=causal, q_offset=q_offset, k_offset=k_offset)
     if workspace is None:

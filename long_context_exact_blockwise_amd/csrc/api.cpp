@@ -192,6 +192,36 @@ int lwm_attn_rope(int32_t B, int32_t H, int32_t S, int32_t D, int32_t dtype, int
                                      static_cast<hipStream_t>(stream)));
 }
 
+// RoPE at load: bf16 with D = 128 only, theta > 1 and finite, positions below 2^32.
+static int check_rope(const lwm_attn_desc* d, double theta) {
+  if (!(theta > 1.0) || theta == std::numeric_limits<double>::infinity()) return LWM_ERR_INVALID_ARG;
+  if (d->dtype != LWM_BF16 || d->D != 128) return LWM_ERR_UNSUPPORTED;
+  if (d->q_offset + int64_t(d->Sq) > (int64_t(1) << 32) || d->k_offset + int64_t(d->Sk) > (int64_t(1) << 32))
+    return LWM_ERR_SHAPE;
+  return LWM_OK;
+}
+
+int lwm_attn_fwd_rope(const lwm_attn_desc* d, int32_t mode, double theta, const void* q,
+                      const void* k_rot, const void* v, const int32_t* seg_q, const int32_t* seg_k,
+                      const void* table, void* o, float* lse, float* m, float* l, float* acc,
+                      void* stream) {
+  int rc = check_attention_desc(d);
+  if (rc) return rc;
+  rc = check_rope(d, theta);
+  if (rc) return rc;
+  if (mode != LWM_OUT_FINAL && mode != LWM_OUT_PARTIAL) return LWM_ERR_INVALID_ARG;
+  if (d->Sq == 0) return LWM_OK;
+  if (!q || !seg_q || !table) return LWM_ERR_INVALID_ARG;
+  if (d->Sk > 0 && (!k_rot || !v || !seg_k)) return LWM_ERR_INVALID_ARG;
+  if (mode == LWM_OUT_FINAL && (!o || !lse)) return LWM_ERR_INVALID_ARG;
+  if (mode == LWM_OUT_PARTIAL && (!m || !l || !acc)) return LWM_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k_rot, v, seg_q, seg_k, table, o, lse, m, l, acc};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return LWM_ERR_ALIGNMENT;
+  return hip_status(lwm::launch_fwd_rope_bf16(*d, mode, theta, q, k_rot, v, seg_q, seg_k, table, o,
+                                              lse, m, l, acc, static_cast<hipStream_t>(stream)));
+}
+
 static int check_packed_loss(int32_t B, int32_t T, int32_t V, int32_t nseg) {
   if (B < 0 || T < 0 || nseg < 1) return LWM_ERR_SHAPE;
   if (V < 8 || V % 8 != 0 || V > 131072) return LWM_ERR_UNSUPPORTED;
@@ -285,6 +315,30 @@ int lwm_attn_bwd(const lwm_attn_desc* d, const void* q, const void* k, const voi
                  void* workspace, size_t ws_bytes, void* stream) {
   return bwd_impl(d, -1, q, k, v, o, dO, lse, seg_q, seg_k, table, dq, dk, dv, workspace,
                   ws_bytes, stream);
+}
+
+int lwm_attn_bwd_rope(const lwm_attn_desc* d, double theta, const void* q, const void* q_rot,
+                      const void* k, const void* k_rot, const void* v, const void* o,
+                      const void* dO, const float* lse, const int32_t* seg_q, const int32_t* seg_k,
+                      const void* table, void* dq, void* dk, void* dv, void* workspace,
+                      size_t ws_bytes, void* stream) {
+  int rc = check_attention_desc(d);
+  if (rc) return rc;
+  rc = check_rope(d, theta);
+  if (rc) return rc;
+  if (d->Sq == 0 || d->Sk == 0)  // no pairs: zero gradients, as without RoPE
+    return bwd_impl(d, -1, q, k, v, o, dO, lse, seg_q, seg_k, table, dq, dk, dv, workspace,
+                    ws_bytes, stream);
+  if (!table || !q || !q_rot || !o || !dO || !lse || !seg_q || !dq) return LWM_ERR_INVALID_ARG;
+  if (!k || !k_rot || !v || !seg_k || !dk || !dv) return LWM_ERR_INVALID_ARG;
+  if (!workspace || ws_bytes < lwm_attn_bwd_workspace_bytes(d)) return LWM_ERR_WORKSPACE;
+  const void* ptrs[] = {q, q_rot, k, k_rot, v, o, dO, lse, seg_q, seg_k, table, dq, dk, dv, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return LWM_ERR_ALIGNMENT;
+  return hip_status(lwm::launch_bwd_rope_bf16(*d, theta, q, q_rot, k, k_rot, v, o, dO, lse, seg_q,
+                                              seg_k, table, dq, dk, dv,
+                                              static_cast<float*>(workspace),
+                                              static_cast<hipStream_t>(stream)));
 }
 
 int lwm_attn_bwd_phase(const lwm_attn_desc* d, int32_t phase, const void* q, const void* k,

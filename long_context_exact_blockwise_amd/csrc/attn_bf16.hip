@@ -27,6 +27,7 @@
 
 #include "common.h"
 #include "mfma_tile.h"
+#include "rope_math.h"
 
 namespace lwm {
 namespace {
@@ -261,6 +262,45 @@ __device__ __forceinline__ void sdp_chain(f32x16& sacc, f32x16& pacc, const uint
   __builtin_amdgcn_sched_group_barrier(0x008, 4, 3);
 }
 
+// RoPE at load (the register-resident operand of a kernel, from unrotated input): the lane's
+// 64 elements of its row at global position pos, element 16 s + 8 hf + j in x[s][j], i.e.
+// pairs 8 s + 4 hf + k, turned and rounded to bf16 exactly as the standalone RoPE kernel does.
+__device__ __forceinline__ void rope_row_bf16(bf16x8* x, int64_t pos, int hf, const RopeFreq& fr) {
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const double rev = hf ? fr.rev[8 * s + 4 + k] : fr.rev[8 * s + k];
+      float c, sn;
+      rope_cs_turns(rope_turn(pos, rev), c, sn);
+      float a = float(x[s][2 * k]), b = float(x[s][2 * k + 1]);
+      rope_turn_pair(a, b, c, sn);
+      x[s][2 * k] = (__bf16)a;
+      x[s][2 * k + 1] = (__bf16)b;
+    }
+}
+
+// RoPE turned back (the transpose) on a float32 accumulator row in the MFMA output layout:
+// slot 4 g + e of block db holds element 32 db + 8 g + 4 hf + e, so slots (4g, 4g+1) and
+// (4g+2, 4g+3) are pairs 16 db + 4 g + 2 hf and that + 1.  The row is at position pos.
+__device__ __forceinline__ void rope_back_acc(f32x16* acc, int64_t pos, int hf, const RopeFreq& fr) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int i = 16 * db + 4 * g + e;
+        const double rev = hf ? fr.rev[i + 2] : fr.rev[i];
+        float c, sn;
+        rope_cs_turns(rope_turn(pos, rev), c, sn);
+        float a = acc[db][4 * g + 2 * e], b = acc[db][4 * g + 2 * e + 1];
+        rope_turn_pair(a, b, c, -sn);
+        acc[db][4 * g + 2 * e] = a;
+        acc[db][4 * g + 2 * e + 1] = b;
+      }
+}
+
 // Wait until this wave's outstanding vector-memory loads (including loads into LDS) are done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -276,7 +316,6 @@ __device__ __forceinline__ void canary_sync() {
 #endif
 }
 
-
 // ---------------------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------------------
@@ -284,9 +323,12 @@ __device__ __forceinline__ void canary_sync() {
 // kSplit (decode): blockIdx.y selects a slice of split_tiles key tiles; the workgroup's
 // PARTIAL state for that slice goes to slice blockIdx.y of (Mo, Lo, ACC), each slice holding
 // B*H*Sq rows; waves whose 32 query rows all lie past Sq only help load tiles.
-template <bool kSplit>
+// kRope: Q arrives unrotated and is turned by RoPE at its global positions as it is loaded;
+// K arrives turned already (the standalone RoPE kernel's output).
+template <bool kSplit, bool kRope = false>
 __device__ __forceinline__ void fwd_bf16_body(AttnParams p, TableView t, int mode, int nqt,
-                                              int split_tiles, const uint16_t* __restrict__ Q,
+                                              int split_tiles, const RopeFreq* rf,
+                                              const uint16_t* __restrict__ Q,
                                               const uint16_t* __restrict__ K,
                                               const uint16_t* __restrict__ V,
                                               const int32_t* __restrict__ seg_q,
@@ -325,6 +367,7 @@ __device__ __forceinline__ void fwd_bf16_body(AttnParams p, TableView t, int mod
     if (qlive) v = gload16(Qh + int64_t(qrow) * D + 16 * s + 8 * hf);
     qreg[s] = *reinterpret_cast<bf16x8*>(&v);
   }
+  if constexpr (kRope) rope_row_bf16(qreg, p.q_offset + qrow, hf, *rf);
   const int32_t sq = qlive ? seg_q[int64_t(b) * p.Sq + qrow] : -1;
   const int dpos = clamp_dpos(p.q_offset, p.k_offset);
 
@@ -546,7 +589,16 @@ fwd_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __
                 const int32_t* __restrict__ seg_q, const int32_t* __restrict__ seg_k,
                 uint16_t* __restrict__ O, float* __restrict__ LSE, float* __restrict__ Mo,
                 float* __restrict__ Lo, float* __restrict__ ACC) {
-  fwd_bf16_body<false>(p, t, mode, nqt, 0, Q, K, V, seg_q, seg_k, O, LSE, Mo, Lo, ACC);
+  fwd_bf16_body<false>(p, t, mode, nqt, 0, nullptr, Q, K, V, seg_q, seg_k, O, LSE, Mo, Lo, ACC);
+}
+
+__global__ void __launch_bounds__(NT, 2)
+fwd_rope_bf16_kernel(AttnParams p, TableView t, int mode, int nqt, const uint16_t* __restrict__ Q,
+                     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                     const int32_t* __restrict__ seg_q, const int32_t* __restrict__ seg_k,
+                     uint16_t* __restrict__ O, float* __restrict__ LSE, float* __restrict__ Mo,
+                     float* __restrict__ Lo, float* __restrict__ ACC, RopeFreq rf) {
+  fwd_bf16_body<false, true>(p, t, mode, nqt, 0, &rf, Q, K, V, seg_q, seg_k, O, LSE, Mo, Lo, ACC);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -559,7 +611,7 @@ decode_bf16_kernel(AttnParams p, TableView t, int nqt, int split_tiles,
                    const uint16_t* __restrict__ V, const int32_t* __restrict__ seg_q,
                    const int32_t* __restrict__ seg_k, float* __restrict__ Mo,
                    float* __restrict__ Lo, float* __restrict__ ACC) {
-  fwd_bf16_body<true>(p, t, LWM_OUT_PARTIAL, nqt, split_tiles, Q, K, V, seg_q, seg_k, nullptr,
+  fwd_bf16_body<true>(p, t, LWM_OUT_PARTIAL, nqt, split_tiles, nullptr, Q, K, V, seg_q, seg_k, nullptr,
                       nullptr, Mo, Lo, ACC);
 }
 
@@ -665,12 +717,19 @@ __global__ void __launch_bounds__(NT) delta_bf16_kernel(int64_t rows, const uint
 
 // dQ: query-major like the forward.  Per key tile: S^T = K Q^T, dP^T = V dO^T,
 // dS^T = P^T (dP^T - Delta), dQ^T += K^T dS^T (K^T read transposed from the K tile).
-__global__ void __launch_bounds__(NT, 2)
-dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ Q,
-               const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-               const uint16_t* __restrict__ dO, const float* __restrict__ LSE2,
-               const float* __restrict__ delta, const int32_t* __restrict__ seg_q,
-               const int32_t* __restrict__ seg_k, uint16_t* __restrict__ dQ) {
+// kRope: Q arrives unrotated and is turned at load, K arrives turned, and dQ (the gradient
+// of the turned Q) is turned back in float32 before it is rounded: the gradient of Q.
+template <bool kRope>
+__device__ __forceinline__ void dq_bf16_body(AttnParams p, TableView t, int nqt, const RopeFreq* rf,
+                                             const uint16_t* __restrict__ Q,
+                                             const uint16_t* __restrict__ K,
+                                             const uint16_t* __restrict__ V,
+                                             const uint16_t* __restrict__ dO,
+                                             const float* __restrict__ LSE2,
+                                             const float* __restrict__ delta,
+                                             const int32_t* __restrict__ seg_q,
+                                             const int32_t* __restrict__ seg_k,
+                                             uint16_t* __restrict__ dQ) {
   // [K tile | V tile] per buffer half in one array, so V reads reuse the K read addresses
   // with a constant offset
   __shared__ __attribute__((aligned(16))) uint16_t kv_lds[4 * kTileElems];
@@ -708,6 +767,7 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
     qreg[s] = *reinterpret_cast<bf16x8*>(&a);
     greg[s] = *reinterpret_cast<bf16x8*>(&g);
   }
+  if constexpr (kRope) rope_row_bf16(qreg, p.q_offset + qrow, hf, *rf);
   const float lse2 = qlive ? LSE2[r64] : 0.f;
   const float ndl = qlive ? delta[r64] : 0.f;  // -Delta of the lane's row
   const int32_t sq = qlive ? seg_q[int64_t(b) * p.Sq + qrow] : -1;
@@ -833,13 +893,41 @@ dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ 
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
+    for (int i = 0; i < 16; ++i) dqacc[db][i] *= p.scale;
+  if constexpr (kRope) {
+    // the rows' positions from scalars as well (q_offset + rbase - bh Sq is row 0's)
+    int64_t pos0 = p.q_offset + qt * BQ + wave * 32;
+    asm volatile("" : "+s"(pos0));
+    rope_back_acc(dqacc, pos0 + col, hf, *rf);
+  }
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d0 = 32 * db + 8 * g + 4 * hf;
       __bf16 o4[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(dqacc[db][4 * g + e] * p.scale);
+      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)dqacc[db][4 * g + e];
       *reinterpret_cast<uint2*>(out + d0) = *reinterpret_cast<uint2*>(o4);
     }
+}
+
+__global__ void __launch_bounds__(NT, 2)
+dq_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ Q,
+               const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+               const uint16_t* __restrict__ dO, const float* __restrict__ LSE2,
+               const float* __restrict__ delta, const int32_t* __restrict__ seg_q,
+               const int32_t* __restrict__ seg_k, uint16_t* __restrict__ dQ) {
+  dq_bf16_body<false>(p, t, nqt, nullptr, Q, K, V, dO, LSE2, delta, seg_q, seg_k, dQ);
+}
+
+__global__ void __launch_bounds__(NT, 2)
+dq_rope_bf16_kernel(AttnParams p, TableView t, int nqt, const uint16_t* __restrict__ Q,
+                    const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                    const uint16_t* __restrict__ dO, const float* __restrict__ LSE2,
+                    const float* __restrict__ delta, const int32_t* __restrict__ seg_q,
+                    const int32_t* __restrict__ seg_k, uint16_t* __restrict__ dQ, RopeFreq rf) {
+  dq_bf16_body<true>(p, t, nqt, &rf, Q, K, V, dO, LSE2, delta, seg_q, seg_k, dQ);
 }
 
 // dK/dV accumulation into AGPRs.  The dK/dV kernel needs more than 256 registers; built
@@ -861,13 +949,19 @@ __device__ __forceinline__ void mfma_agpr_fence(f32x16* x, f32x16* y) {
 // dK, dV: key-major.  Workgroup = 128 keys (32 per wave) held in registers; query tiles of
 // 64 stream through LDS.  Per 32-query half: S = Q K^T, dP = dO V^T, P = exp(S - LSE),
 // dS = P (dP - Delta), dV^T += dO^T P, dK^T += Q^T dS (dO^T, Q^T read transposed).
-__global__ void __launch_bounds__(NT, 1)
-dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__ Q,
-                const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-                const uint16_t* __restrict__ dO, const float* __restrict__ LSE2,
-                const float* __restrict__ delta, const int32_t* __restrict__ seg_q,
-                const int32_t* __restrict__ seg_k, uint16_t* __restrict__ dK,
-                uint16_t* __restrict__ dV) {
+// kRope: K arrives unrotated and is turned at load, Q arrives turned, and dK is turned back
+// in float32 before it is rounded.
+template <bool kRope>
+__device__ __forceinline__ void dkv_bf16_body(AttnParams p, TableView t, int nkt, const RopeFreq* rf,
+                                              const uint16_t* __restrict__ Q,
+                                              const uint16_t* __restrict__ K,
+                                              const uint16_t* __restrict__ V,
+                                              const uint16_t* __restrict__ dO,
+                                              const float* __restrict__ LSE2,
+                                              const float* __restrict__ delta,
+                                              const int32_t* __restrict__ seg_q,
+                                              const int32_t* __restrict__ seg_k,
+                                              uint16_t* __restrict__ dK, uint16_t* __restrict__ dV) {
   // [Q tile | dO tile] per buffer half in one array, so dO reads reuse the Q read addresses
   // with a constant offset
   __shared__ __attribute__((aligned(16))) uint16_t qg_lds[4 * kTileElems];
@@ -906,6 +1000,7 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
     kreg[s] = *reinterpret_cast<bf16x8*>(&a);
     vreg[s] = *reinterpret_cast<bf16x8*>(&v);
   }
+  if constexpr (kRope) rope_row_bf16(kreg, p.k_offset + key, hf, *rf);
   const int32_t sk = klive ? seg_k[int64_t(b) * p.Sk + key] : -2;
   const int dpos = clamp_dpos(p.q_offset, p.k_offset);
 
@@ -1064,6 +1159,12 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
   if (!klive) return;
   uint16_t* ko = dK + k64 * D;
   uint16_t* vo = dV + k64 * D;
+  f32x16 dks[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dks[db][i] = dkacc[db][i] * p.scale;
+  if constexpr (kRope) rope_back_acc(dks, p.k_offset + key, hf, *rf);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -1072,12 +1173,32 @@ dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__
       __bf16 k4[4], v4[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        k4[e] = (__bf16)(dkacc[db][4 * g + e] * p.scale);
+        k4[e] = (__bf16)dks[db][4 * g + e];
         v4[e] = (__bf16)(dvacc[db][4 * g + e]);
       }
       *reinterpret_cast<uint2*>(ko + d0) = *reinterpret_cast<uint2*>(k4);
       *reinterpret_cast<uint2*>(vo + d0) = *reinterpret_cast<uint2*>(v4);
     }
+}
+
+__global__ void __launch_bounds__(NT, 1)
+dkv_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__ Q,
+                const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                const uint16_t* __restrict__ dO, const float* __restrict__ LSE2,
+                const float* __restrict__ delta, const int32_t* __restrict__ seg_q,
+                const int32_t* __restrict__ seg_k, uint16_t* __restrict__ dK,
+                uint16_t* __restrict__ dV) {
+  dkv_bf16_body<false>(p, t, nkt, nullptr, Q, K, V, dO, LSE2, delta, seg_q, seg_k, dK, dV);
+}
+
+__global__ void __launch_bounds__(NT, 1)
+dkv_rope_bf16_kernel(AttnParams p, TableView t, int nkt, const uint16_t* __restrict__ Q,
+                     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                     const uint16_t* __restrict__ dO, const float* __restrict__ LSE2,
+                     const float* __restrict__ delta, const int32_t* __restrict__ seg_q,
+                     const int32_t* __restrict__ seg_k, uint16_t* __restrict__ dK,
+                     uint16_t* __restrict__ dV, RopeFreq rf) {
+  dkv_bf16_body<true>(p, t, nkt, &rf, Q, K, V, dO, LSE2, delta, seg_q, seg_k, dK, dV);
 }
 
 }  // namespace
@@ -1093,6 +1214,49 @@ hipError_t launch_fwd_bf16(const lwm_attn_desc& d, int mode, const void* q, cons
       attn_params(d), t, mode, nqt, static_cast<const uint16_t*>(q),
       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), seg_q, seg_k,
       static_cast<uint16_t*>(o), lse, m, l, acc);
+  return hipGetLastError();
+}
+
+// Forward with RoPE at load: q unrotated, k turned already.
+hipError_t launch_fwd_rope_bf16(const lwm_attn_desc& d, int mode, double theta, const void* q,
+                                const void* k, const void* v, const int32_t* seg_q,
+                                const int32_t* seg_k, const void* table, void* o, float* lse,
+                                float* m, float* l, float* acc, hipStream_t stream) {
+  const TableView t = table_view(d, table);
+  const int nqt = (d.Sq + BQ - 1) / BQ;
+  const int64_t grid = int64_t(nqt) * d.H * d.B;
+  fwd_rope_bf16_kernel<<<dim3(unsigned(grid)), dim3(NT), 0, stream>>>(
+      attn_params(d), t, mode, nqt, static_cast<const uint16_t*>(q),
+      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), seg_q, seg_k,
+      static_cast<uint16_t*>(o), lse, m, l, acc, rope_freqs(D, theta));
+  return hipGetLastError();
+}
+
+// Backward with RoPE at load: the dQ pass takes q unrotated and k turned, the dK/dV pass k
+// unrotated and q turned (q_rot); dq and dk are the gradients of the unrotated q and k.
+hipError_t launch_bwd_rope_bf16(const lwm_attn_desc& d, double theta, const void* q,
+                                const void* q_rot, const void* k, const void* k_rot, const void* v,
+                                const void* o, const void* dO, const float* lse,
+                                const int32_t* seg_q, const int32_t* seg_k, const void* table,
+                                void* dq, void* dk, void* dv, float* workspace, hipStream_t stream) {
+  const TableView t = table_view(d, table);
+  const AttnParams p = attn_params(d);
+  const RopeFreq fr = rope_freqs(D, theta);
+  const int64_t rows = int64_t(d.B) * d.H * d.Sq;
+  float* delta = workspace;
+  float* lse2 = workspace + align256(size_t(rows) * sizeof(float)) / sizeof(float);
+  delta_bf16_kernel<<<dim3(unsigned((rows * 16 + NT - 1) / NT)), dim3(NT), 0, stream>>>(
+      rows, static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dO), lse, delta, lse2);
+  const int nqt = (d.Sq + BQ - 1) / BQ;
+  dq_rope_bf16_kernel<<<dim3(unsigned(int64_t(nqt) * d.H * d.B)), dim3(NT), 0, stream>>>(
+      p, t, nqt, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_rot),
+      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), lse2, delta, seg_q, seg_k,
+      static_cast<uint16_t*>(dq), fr);
+  const int nkt = (d.Sk + 127) / 128;
+  dkv_rope_bf16_kernel<<<dim3(unsigned(int64_t(nkt) * d.H * d.B)), dim3(NT), 0, stream>>>(
+      p, t, nkt, static_cast<const uint16_t*>(q_rot), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), lse2, delta, seg_q, seg_k,
+      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), fr);
   return hipGetLastError();
 }
 

@@ -154,6 +154,19 @@ hipError_t launch_fwd_bf16(const lwm_attn_desc& d, int mode, const void* q, cons
                            const void* table, void* o, float* lse, float* m, float* l,
                            float* acc, hipStream_t stream);
 
+// RoPE at load (bf16, D = 128): q unrotated, k turned by the standalone RoPE kernel.
+hipError_t launch_fwd_rope_bf16(const lwm_attn_desc& d, int mode, double theta, const void* q,
+                                const void* k, const void* v, const int32_t* seg_q,
+                                const int32_t* seg_k, const void* table, void* o, float* lse,
+                                float* m, float* l, float* acc, hipStream_t stream);
+
+// Backward with RoPE at load; the workspace as for launch_bwd_bf16.
+hipError_t launch_bwd_rope_bf16(const lwm_attn_desc& d, double theta, const void* q,
+                                const void* q_rot, const void* k, const void* k_rot, const void* v,
+                                const void* o, const void* dO, const float* lse,
+                                const int32_t* seg_q, const int32_t* seg_k, const void* table,
+                                void* dq, void* dk, void* dv, float* workspace, hipStream_t stream);
+
 // Slice states in `workspace` laid out as L (decode_layout or decode_layout_capped).
 hipError_t launch_decode_bf16(const lwm_attn_desc& d, const DecodeLayout& L, const void* q,
                               const void* k, const void* v, const int32_t* seg_q,

@@ -9,9 +9,11 @@
 // Precision.  At theta = 5e7 and p near 2^20 the angle of the fastest pair is about 10^6
 // radians; a float32 product p * w_i would already be off by several hundredths of a radian.
 // So the angle is formed in float64 as revolutions, t = p * w_i / (2 pi), whose fractional
-// part t - rint(t) is exact in float64; only that fraction in [-1/2, 1/2] goes to float32,
-// and sin/cos of (2 pi * fraction) come from sincospi.  The angle error stays below 1e-6
-// radian for every position below 2^32.
+// part t - rint(t) is exact in float64; only that fraction in [-1/2, 1/2] goes to float32
+// (rope_math.h, shared with the attention kernels that rotate Q or K at load, so both turn a
+// pair by the same angle and round alike).  cos and sin of 2 pi * fraction come from the
+// hardware units for bf16 data and from sincospi for float32 data.  The angle error stays
+// below 1e-6 radian for every position below 2^32.
 //
 // Work split.  The kernel streams the tensor once (HBM bound).  A thread owns 8 consecutive
 // elements (4 pairs) at one position; a position's D elements take D/8 threads, and the grid
@@ -26,13 +28,13 @@
 #include <cmath>
 
 #include "common.h"
+#include "rope_math.h"
 
 namespace lwm {
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int64_t kRowsPerThread = 4;  // (batch, head) rows per thread and position
-constexpr double kInv2Pi = 0.15915494309189533577;
 
 __device__ __forceinline__ void load8(const uint16_t* p, float* v) {
   const uint4 u = *reinterpret_cast<const uint4*>(p);
@@ -63,7 +65,7 @@ __device__ __forceinline__ void store8(float* p, const float* v) {
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
 rope_kernel(int64_t BH, int64_t rpt, int32_t S, int32_t D, int32_t tpr_shift, int64_t pos0,
-            double log2_theta, float dir, const T* x, T* y) {  // x and y may be the same buffer
+            RopeFreq fr, float dir, const T* x, T* y) {  // x and y may be the same buffer
   // D / 8 = 2^tpr_shift threads per position, a divisor of kThreads
   const int64_t total = int64_t(S) << tpr_shift;
   const int64_t stride = int64_t(gridDim.x) * kThreads;
@@ -72,7 +74,7 @@ rope_kernel(int64_t BH, int64_t rpt, int32_t S, int32_t D, int32_t tpr_shift, in
   // revolutions per position of this thread's pairs: theta^(-2i/D) / (2 pi)
   double rev[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) rev[k] = exp2(-double(2 * (4 * part + k)) / D * log2_theta) * kInv2Pi;
+  for (int k = 0; k < 4; ++k) rev[k] = fr.rev[4 * part + k];
   const int64_t rstride = int64_t(S) * D;  // from one (batch, head) row block to the next
   // this workgroup's share of the batch rows and heads: rpt of them
   const int64_t bh0 = int64_t(blockIdx.y) * rpt;
@@ -82,13 +84,14 @@ rope_kernel(int64_t BH, int64_t rpt, int32_t S, int32_t D, int32_t tpr_shift, in
   y += bh0 * rstride;
   for (; g < total; g += stride) {
     const int64_t s = g >> tpr_shift;
-    const double pos = double(pos0 + s);
     float cs[4], sn[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const double t = pos * rev[k];
-      const float f = float(t - rint(t));  // fraction of a turn, |f| <= 1/2
-      sincospif(2.f * f, &sn[k], &cs[k]);
+      const float f = rope_turn(pos0 + s, rev[k]);  // fraction of a turn, |f| <= 1/2
+      if constexpr (sizeof(T) == 2)
+        rope_cs_turns(f, cs[k], sn[k]);
+      else
+        sincospif(2.f * f, &sn[k], &cs[k]);
       sn[k] *= dir;
     }
     // every batch row and head shares the position, hence the angles
@@ -96,11 +99,7 @@ rope_kernel(int64_t BH, int64_t rpt, int32_t S, int32_t D, int32_t tpr_shift, in
     T* ys = y + s * D + 8 * part;
     auto turn = [&](float* v) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float a = v[2 * k], b = v[2 * k + 1];
-        v[2 * k] = a * cs[k] - b * sn[k];
-        v[2 * k + 1] = a * sn[k] + b * cs[k];
-      }
+      for (int k = 0; k < 4; ++k) rope_turn_pair(v[2 * k], v[2 * k + 1], cs[k], sn[k]);
     };
     const int64_t n = bh1 - bh0;
     for (int64_t bh = 0; bh < n; ++bh) {
@@ -123,17 +122,17 @@ hipError_t launch_rope(int32_t B, int32_t H, int32_t S, int32_t D, int32_t dtype
   int64_t rpt = kRowsPerThread;
   if ((bh + rpt - 1) / rpt > 65535) rpt = (bh + 65534) / 65535;  // the grid's y extent
   const int64_t groups = (bh + rpt - 1) / rpt;
-  const double l2t = std::log2(theta);
+  const RopeFreq fr = rope_freqs(D, theta);
   const float dir = inverse ? -1.f : 1.f;
   int shift = 0;
   while ((8 << shift) < D) ++shift;
   if (dtype == LWM_BF16)
     rope_kernel<uint16_t><<<dim3(unsigned(blocks), unsigned(groups)), dim3(kThreads), 0, stream>>>(
-        bh, rpt, S, D, shift, pos0, l2t, dir, static_cast<const uint16_t*>(x),
+        bh, rpt, S, D, shift, pos0, fr, dir, static_cast<const uint16_t*>(x),
         static_cast<uint16_t*>(y));
   else
     rope_kernel<float><<<dim3(unsigned(blocks), unsigned(groups)), dim3(kThreads), 0, stream>>>(
-        bh, rpt, S, D, shift, pos0, l2t, dir, static_cast<const float*>(x),
+        bh, rpt, S, D, shift, pos0, fr, dir, static_cast<const float*>(x),
         static_cast<float*>(y));
   return hipGetLastError();
 }

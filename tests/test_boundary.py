@@ -333,3 +333,30 @@ def test_python_wrappers_check_buffer_sizes():
         lwm.lwm_attn_decode(d, q, k, k, sq, sk, tab, o, lse[:, :1], None)
     with pytest.raises(ValueError, match="o has"):
         lwm.lwm_attn_decode_noalloc(d, q, k, k, sq, sk, tab, k, lse)
+
+
+def test_rope_at_load_rejects_bad_arguments(lib):
+    fwd, bwd = lib.lwm_attn_fwd_rope, lib.lwm_attn_bwd_rope
+
+    def cf(d, theta=1e6, mode=0, **kw):
+        names = ("q", "k", "v", "sq", "sk", "t", "o", "lse", "m", "l", "acc")
+        return fwd(ctypes.byref(d), mode, theta, *[kw.get(n, FAKE) for n in names], None)
+
+    def cb(d, theta=1e6, ws_bytes=1 << 30, **kw):
+        names = ("q", "qr", "k", "kr", "v", "o", "do", "lse", "sq", "sk", "t", "dq", "dk", "dv", "ws")
+        return bwd(ctypes.byref(d), theta, *[kw.get(n, FAKE) for n in names], ws_bytes, None)
+
+    for call in (cf, cb):
+        assert call(desc(D=64, dtype=lwm.LWM_F32)) == UNSUP   # RoPE at load: bf16, D = 128
+        assert call(desc(D=64)) == UNSUP
+        assert call(desc(), theta=1.0) == INVALID
+        assert call(desc(), theta=float("inf")) == INVALID
+        assert call(desc(q_offset=(1 << 32) - 255)) == SHAPE    # positions beyond 2^32
+        assert call(desc(k_offset=(1 << 32) - 100)) == SHAPE
+    assert cf(desc(), mode=2) == INVALID
+    assert cf(desc(), k=None) == INVALID
+    assert cf(desc(), v=FAKE + 8) == ALIGN
+    assert cb(desc(), qr=None) == INVALID
+    assert cb(desc(), kr=FAKE + 4) == ALIGN
+    assert cb(desc(), ws=None) == WS
+    assert cb(desc(), ws_bytes=lwm.lwm_attn_bwd_workspace_bytes(desc()) - 1) == WS

@@ -146,8 +146,13 @@ def test_rope_packed_128k_sampled_rows():
     k = li.device_normal((w.B, w.H, w.Sk, w.D), w.seed, w.value_scale, 1, torch.bfloat16, "cuda")
     v = li.device_normal((w.B, w.H, w.Sk, w.D), w.seed, w.value_scale, 2, torch.bfloat16, "cuda")
     qr, kr = lwm.rope(q, 0, theta), lwm.rope(k, 0, theta)
-    o, lse, _ = lwm.attention_forward(qr, kr, v, seg_dev(seg_q), seg_dev(seg_k))
+    o, lse, table = lwm.attention_forward(qr, kr, v, seg_dev(seg_q), seg_dev(seg_k))
+    # RoPE inside the forward's Q load: the same bits as turning Q first
+    o2, lse2, _ = lwm.attention_forward(q, k, v, seg_dev(seg_q), seg_dev(seg_k), table=table,
+                                        rope_theta=theta)
     torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    del o2, lse2
     pos = np.arange(w.Sq)
     worst_rot = -1.0
     samples = li.sample_rows(w, lengths)
@@ -167,3 +172,56 @@ def test_rope_packed_128k_sampled_rows():
     say(f"  rotation excess over bound {worst_rot:.1e}; sampled rows O {worst[0]:.2e} LSE {worst[1]:.2e}")
     assert worst_rot <= 0
     assert worst[0] <= TOL_O["bf16"] and worst[1] <= TOL_LSE
+
+
+@pytest.mark.parametrize("case", [("packed", 31, 1, 2, 900, 900, 0, 0, 1e7, "packed"),
+                                  ("ring_chunk_offsets", 32, 1, 1, 384, 448, 900000, 899000, 5e7, "single"),
+                                  ("padded_b2", 33, 2, 2, 700, 700, 0, 0, 1e6, "padded")],
+                         ids=["packed", "ring_chunk_offsets", "padded_b2"])
+def test_rope_at_load_equals_rope_first(case):
+    """lwm_attn_fwd_rope / lwm_attn_bwd_rope (Q or K turned inside the kernels' register
+    loads) against lwm_attn_fwd / lwm_attn_bwd on tensors turned first by lwm_attn_rope: the
+    turn at load rounds exactly as the standalone kernel, so O, LSE, the partial state and dV
+    are identical bit for bit; dQ and dK are turned back in float32 before rounding instead
+    of after, so they agree within bf16 rounding, and both against the oracle's composition."""
+    name, seed, B, H, Sq, Sk, q_off, k_off, theta, layout = case
+    say(f"rope at load, case {name}: B={B} H={H} Sq={Sq} Sk={Sk} offs={q_off},{k_off} theta={theta:g}")
+    D = 128
+    x, seg_q, seg_k = make_case(seed, B, H, Sq, Sk, D, "bf16", "single" if layout == "single" else "packed",
+                                q_off, k_off, pad=layout == "padded")
+    q, k, v, do = (to_dev(x[n], "bf16") for n in ("q", "k", "v", "do"))
+    sq, sk = seg_dev(seg_q), seg_dev(seg_k)
+    desc = lwm.make_desc(B, H, Sq, Sk, D, torch.bfloat16, q_offset=q_off, k_offset=k_off)
+    table = lwm.lwm_attn_build_block_table(desc, sq, sk)
+    qr, kr = lwm.rope(q, q_off, theta), lwm.rope(k, k_off, theta)
+    o1, l1 = torch.empty_like(q), torch.empty((B, H, Sq), dtype=torch.float32, device="cuda")
+    o2, l2 = torch.empty_like(q), torch.empty_like(l1)
+    lwm.lwm_attn_fwd(desc, lwm.LWM_OUT_FINAL, qr, kr, v, sq, sk, table, o=o1, lse=l1)
+    lwm.lwm_attn_fwd_rope(desc, lwm.LWM_OUT_FINAL, theta, q, kr, v, sq, sk, table, o=o2, lse=l2)
+    st1 = lwm.attention_partial(qr, kr, v, sq, sk, q_offset=q_off, k_offset=k_off, table=table)
+    st2 = tuple(torch.empty_like(t) for t in st1)
+    lwm.lwm_attn_fwd_rope(desc, lwm.LWM_OUT_PARTIAL, theta, q, kr, v, sq, sk, table, m=st2[0], l=st2[1],
+                          acc=st2[2])
+    ws = torch.empty(lwm.lwm_attn_bwd_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    g1 = [torch.empty_like(t) for t in (q, k, v)]
+    g2 = [torch.empty_like(t) for t in (q, k, v)]
+    lwm.lwm_attn_bwd(desc, qr, kr, v, o1, do, l1, sq, sk, table, *g1, ws)
+    lwm.rope(g1[0], q_off, theta, inverse=True, out=g1[0])
+    lwm.rope(g1[1], k_off, theta, inverse=True, out=g1[1])
+    lwm.lwm_attn_bwd_rope(desc, theta, q, qr, k, kr, v, o2, do, l2, sq, sk, table, *g2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(st1, st2):
+        assert torch.equal(a, b)
+    assert torch.equal(g1[2], g2[2])
+    e_unfused = [max_abs(f64(a), f64(b)) for a, b in zip(g1[:2], g2[:2])]
+    say(f"  O, LSE, partial state, dV identical; dQ, dK vs turned-first path {e_unfused[0]:.1e} {e_unfused[1]:.1e}")
+    # the oracle: attention on the turned inputs (rounded to bf16 as stored), gradients turned back
+    scale = 1 / math.sqrt(D)
+    qf, kf, vf, dof = (host_f64(x[n], "bf16") for n in ("q", "k", "v", "do"))
+    qpos, kpos = q_off + np.arange(Sq), k_off + np.arange(Sk)
+    qrf, krf = stored(R.rotate(qf, qpos, theta), "bf16"), stored(R.rotate(kf, kpos, theta), "bf16")
+    dqr, dkr, dv_ref = A.backward(qrf, krf, vf, dof, seg_q, seg_k, scale, True, q_off, k_off)
+    check_grad("dQ (RoPE at load)", f64(g2[0]), R.rotate(dqr, qpos, theta, inverse=True), "bf16")
+    check_grad("dK (RoPE at load)", f64(g2[1]), R.rotate(dkr, kpos, theta, inverse=True), "bf16")
+    check_grad("dV (RoPE at load)", f64(g2[2]), dv_ref, "bf16")
