@@ -75,7 +75,11 @@ typedef struct {
 /*
  * Block table.  Classifies each (query block, key block) pair so the kernels can skip
  * pairs with no visible key and drop masking where every pair is visible; it is how the
- * causal and packing masks of the pages become skipped work.
+ * causal and packing masks of the pages become skipped work.  The two masks: a packed
+ * sample only attends to itself (LWM deep dive, section "Masked sequence packing", first
+ * step of the recipe) and the model predicts the next token of one sequence (sections
+ * "核心问题" and "模型结构"); the block sizes are the query-chunk knob of the pages' blockwise
+ * attention (0539edu article, section "模型训练关键参数配置": scan_query_chunk_size).
  *   status  uint8 [B][nqb][nkb]: LWM_TILE_SKIP if no pair can be visible (causally empty,
  *           all padding, or disjoint segment-id intervals), LWM_TILE_FULL if the block lies
  *           inside [0,Sq)x[0,Sk) and every pair is visible, else LWM_TILE_PARTIAL.
@@ -111,7 +115,9 @@ int lwm_attn_fwd(const lwm_attn_desc* desc, int32_t mode, const void* q, const v
                  void* o, float* lse, float* m, float* l, float* acc, void* stream);
 
 /*
- * Merge a chunk's partial state into a running state (the ring step's combine): per row
+ * Merge a chunk's partial state into a running state (the ring step's combine; LWM deep
+ * dive, section "RingAttention 为什么必要": each device keeps its query block while key/value
+ * blocks arrive round the ring, and the result is exact full attention): per row
  *   m' = max(m, mc),  l' = l e^(m-m') + lc e^(mc-m'),  acc' = acc e^(m-m') + accc e^(mc-m').
  * An empty side (l = 0) contributes nothing; two empty sides stay empty (-inf, 0, 0).
  * rows = B*H*Sq; m, l, mc, lc are float32 [rows]; acc, accc float32 [rows, D].
@@ -169,7 +175,10 @@ int lwm_attn_decode_noalloc(const lwm_attn_desc* desc, const void* q, const void
 
 /*
  * Backward of the forward above for an upstream gradient dO, recomputing P from the saved
- * LSE (P_ij = exp(s_ij - LSE_i) on visible pairs):
+ * LSE (P_ij = exp(s_ij - LSE_i) on visible pairs).  The pages train the model through this
+ * attention at every context stage (LWM deep dive, sections "大模型训练路线图" and "Stage I：长上下文语言模型",
+ * Tables 11 and 13) but print no gradient; these are the textbook derivatives of the
+ * definition above:
  *   Delta_i = <dO_i, O_i>,  dS_ij = P_ij (<dO_i, v_j> - Delta_i),
  *   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i,
  * sums running over the keys given and the queries given.  o and lse are the forward's

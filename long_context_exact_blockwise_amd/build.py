@@ -63,9 +63,30 @@ def _link(objs, out: str) -> None:
     os.replace(tmp, out)
 
 
+# The compiler the GPU parity suite was last run green with.  The dK/dV kernel's
+# accumulations are inline-asm MFMAs whose hazard wait states are written into the asm, which
+# the compiler's hazard checks do not see; a different compiler may place its own code between
+# them differently, so after a toolchain change the GPU gradient tests must pass again before
+# the library is used.
+VALIDATED_COMPILER = "AMD clang version 22.0.0git (https://github.com/RadeonOpenCompute/llvm-project roc-7.2.0 26014 7b800a19466229b8479a78de19143dc33c3ab9b5)"
+
+
+def compiler_version() -> str:
+    r = subprocess.run([HIPCC, "--version"], capture_output=True, text=True)
+    for line in r.stdout.splitlines():
+        if "clang version" in line:
+            return line.strip()
+    return r.stdout.strip()
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source, link the shared library and its race-canary twin; returns the
     library's path."""
+    seen = compiler_version()
+    if seen != VALIDATED_COMPILER:
+        print(f"WARNING: building with\n  {seen}\nbut the GPU parity suite was validated with\n  "
+              f"{VALIDATED_COMPILER}\nrun `pytest tests -m gpu` before using this build (the dK/dV "
+              "kernel's asm MFMAs carry hand-written hazard waits)", file=sys.stderr, flush=True)
     os.makedirs(BUILD, exist_ok=True)
     jobs = [(src, (), "") for src in SOURCES]
     jobs += [(src, tuple(flags), ".canary") for src, flags in CANARY_SOURCES.items()]
