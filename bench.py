@@ -471,6 +471,8 @@ def main() -> int:
                     help="skip the decode and packed-loss parts")
     ap.add_argument("--decode-unsplit", action="store_true",
                     help="also time the plain forward on the decode inputs")
+    ap.add_argument("--probes", action="store_true",
+                    help="only run the gfx950 microbenchmarks of tests/probes (one JSON record)")
     ap.add_argument("--configs", action="store_true",
                     help="only time each of the five workloads (one JSON record per workload)")
     ap.add_argument("--config-reps", type=int, default=10)
@@ -502,6 +504,12 @@ def main() -> int:
                           "launches": 3}))
         return 0
     lwm.load_library()
+    if args.probes:
+        sys.path.insert(0, os.path.join(ROOT, "tests", "probes"))
+        import probes_lib
+
+        print(json.dumps({"probes": probes_lib.run(torch)}), flush=True)
+        return 0
     if args.configs:
         config_table(lwm, li, torch, args.config_reps)
         return 0
