@@ -299,6 +299,22 @@ const char* lwm_attn_status_string(int status);
 /* Library version as major*10000 + minor*100 + patch. */
 int lwm_attn_version(void);
 
+/* Device checks of a debug build (the library compiled with LWM_DEBUG, built beside the
+ * normal one as liblwm_attn_debug.so).  No passage of the pages defines it: it is for tests
+ * and for callers chasing a wrong table or launch.  In such a build every kernel checks the
+ * indices it derives from the block table (query and key ranges, tile statuses, status-chunk
+ * slots) and from its launch shape against the extents it indexes, and the merge checks that
+ * an empty state carries l = 0; a failed check does not trap, it is recorded on the device.
+ *   words  host uint32_t[2], written: words[0] has bit c set for every failed check code c
+ *          since the last call (codes 1-18, listed in the library's sources; 31 is the self
+ *          test), words[1] = code << 24 | workgroup of the first failure, or 0.
+ *   flags  0, or LWM_DEBUG_SELF_TEST to fail check 31 once on purpose before reading.
+ * Synchronises the current device, then reads and clears the records.  Returns
+ * LWM_ERR_UNSUPPORTED (words zeroed) in a library built without LWM_DEBUG, LWM_ERR_INVALID_ARG
+ * for a NULL words or unknown flags, LWM_ERR_HIP if the synchronisation or a copy fails. */
+#define LWM_DEBUG_SELF_TEST 1
+int lwm_attn_debug_status(uint32_t* words, int32_t flags);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,8 +30,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 # LWM_ATTN_LIBRARY names another build of the same library (the host-sanitizer build of the
 # boundary tests); by default the in-tree build is loaded
 LIB_PATH = os.environ.get("LWM_ATTN_LIBRARY") or os.path.join(_PKG, "liblwm_attn.so")
-# the race-canary build of the bf16 kernels (see build.py)
+# the race-canary build of the bf16 kernels and the build with device checks (see build.py)
 CANARY_LIB_PATH = os.path.join(_PKG, "liblwm_attn_canary.so")
+DEBUG_LIB_PATH = os.path.join(_PKG, "liblwm_attn_debug.so")
 
 LWM_BF16, LWM_F32 = 0, 1
 LWM_OUT_FINAL, LWM_OUT_PARTIAL = 0, 1
@@ -49,8 +50,9 @@ EXPORTED = (
     "lwm_attn_bwd_phase", "lwm_attn_status_string", "lwm_attn_version",
     "lwm_attn_decode_workspace_bytes", "lwm_attn_decode", "lwm_attn_rope",
     "lwm_attn_packed_loss_workspace_bytes", "lwm_attn_packed_loss", "lwm_attn_decode_noalloc",
-    "lwm_attn_fwd_rope", "lwm_attn_bwd_rope",
+    "lwm_attn_fwd_rope", "lwm_attn_bwd_rope", "lwm_attn_debug_status",
 )
+LWM_DEBUG_SELF_TEST = 1
 DECODE_SCRATCH_BYTES = 64 << 20  # LWM_DECODE_SCRATCH_BYTES
 LWM_BWD_DELTA, LWM_BWD_DQ, LWM_BWD_DKV = 0, 1, 2
 
@@ -127,6 +129,7 @@ def _open_library(path: str):
                                                 P, P, SZ, P]),
         "lwm_attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "lwm_attn_version": (ctypes.c_int, []),
+        "lwm_attn_debug_status": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32), I32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -134,6 +137,14 @@ def _open_library(path: str):
         fn.argtypes = args
     _opened[path] = lib
     return lib
+
+
+def lwm_attn_debug_status(self_test: bool = False) -> Tuple[int, int, int]:
+    """(status, words[0], words[1]) of the library's device-check records, read and cleared
+    (lwm_attn_debug_status); status is LWM_ERR_UNSUPPORTED (-4) for a build without checks."""
+    w = (ctypes.c_uint32 * 2)()
+    rc = load_library().lwm_attn_debug_status(w, LWM_DEBUG_SELF_TEST if self_test else 0)
+    return rc, int(w[0]), int(w[1])
 
 
 def _check(call: str, rc: int):

@@ -40,6 +40,11 @@ SOURCE_FLAGS = {"attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 # tests compare bit for bit with the normal one.
 CANARY_LIB = os.path.join(PKG, "liblwm_attn_canary.so")
 CANARY_SOURCES = {"attn_bf16.hip": ["-DLWM_RACE_CANARY"]}
+# Every source again with the device checks of LWM_DEBUG (indices derived from the block table
+# checked against the extents they index, failures recorded on the device and read back by
+# lwm_attn_debug_status), linked into a third library for the tests.
+DEBUG_LIB = os.path.join(PKG, "liblwm_attn_debug.so")
+DEBUG_FLAGS = ["-DLWM_DEBUG"]
 
 
 def _compile(src: str, extra=(), suffix: str = "") -> str:
@@ -80,26 +85,29 @@ def compiler_version() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source, link the shared library and its race-canary twin; returns the
-    library's path."""
+    """Compile every source, link the shared library, its race-canary twin and its build with
+    device checks; returns the library's path."""
     seen = compiler_version()
     if seen != VALIDATED_COMPILER:
         print(f"WARNING: building with\n  {seen}\nbut the GPU parity suite was validated with\n  "
               f"{VALIDATED_COMPILER}\nrun `pytest tests -m gpu` before using this build (the dK/dV "
               "kernel's asm MFMAs carry hand-written hazard waits)", file=sys.stderr, flush=True)
     os.makedirs(BUILD, exist_ok=True)
+    n = len(SOURCES)
     jobs = [(src, (), "") for src in SOURCES]
+    jobs += [(src, tuple(DEBUG_FLAGS), ".debug") for src in SOURCES]
     jobs += [(src, tuple(flags), ".canary") for src, flags in CANARY_SOURCES.items()]
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         objs = list(ex.map(lambda j: _compile(*j), jobs))
-    normal = objs[:len(SOURCES)]
+    normal, debug = objs[:n], objs[n:2 * n]
     canary = [o for o in normal]
-    for (src, _, _), o in zip(jobs[len(SOURCES):], objs[len(SOURCES):]):
+    for (src, _, _), o in zip(jobs[2 * n:], objs[2 * n:]):
         canary[SOURCES.index(src)] = o
     _link(normal, LIB)
     _link(canary, CANARY_LIB)
+    _link(debug, DEBUG_LIB)
     if verbose:
-        print(f"built {LIB} and {CANARY_LIB}")
+        print(f"built {LIB}, {CANARY_LIB} and {DEBUG_LIB}")
     return LIB
 
 

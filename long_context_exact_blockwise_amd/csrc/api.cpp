@@ -46,7 +46,18 @@ int check_attention_desc(const lwm_attn_desc* d) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LWM_OK : LWM_ERR_HIP; }
 
+#ifdef LWM_DEBUG
+// One failed check on purpose (code kChkSelfTest), so that a test can see the reporting work.
+__global__ void debug_self_test_kernel() { LWM_CHECK(threadIdx.x != 0, lwm::kChkSelfTest); }
+#endif
+
 }  // namespace
+
+#ifdef LWM_DEBUG
+namespace lwm {
+LWM_DEBUG_READER(api)
+}  // namespace lwm
+#endif
 
 extern "C" {
 
@@ -348,6 +359,30 @@ int lwm_attn_bwd_phase(const lwm_attn_desc* d, int32_t phase, const void* q, con
   if (phase < 0) return LWM_ERR_INVALID_ARG;
   return bwd_impl(d, phase, q, k, v, o, dO, lse, seg_q, seg_k, table, dq, dk, dv, workspace,
                   ws_bytes, stream);
+}
+
+int lwm_attn_debug_status(uint32_t* words, int32_t flags) {
+  if (words == nullptr || (flags & ~LWM_DEBUG_SELF_TEST) != 0) return LWM_ERR_INVALID_ARG;
+  words[0] = words[1] = 0;
+#ifdef LWM_DEBUG
+  if (hipDeviceSynchronize() != hipSuccess) return LWM_ERR_HIP;
+  if (flags & LWM_DEBUG_SELF_TEST) {
+    debug_self_test_kernel<<<1, 64>>>();
+    if (hipGetLastError() != hipSuccess || hipDeviceSynchronize() != hipSuccess) return LWM_ERR_HIP;
+  }
+  hipError_t (*const readers[])(unsigned*) = {lwm::debug_read_attn_bf16, lwm::debug_read_attn_f32,
+                                               lwm::debug_read_table, lwm::debug_read_merge,
+                                               lwm::debug_read_api};
+  for (auto rd : readers) {
+    unsigned w[2] = {0u, 0u};
+    if (rd(w) != hipSuccess) return LWM_ERR_HIP;
+    words[0] |= w[0];
+    if (words[1] == 0) words[1] = w[1];
+  }
+  return LWM_OK;
+#else
+  return LWM_ERR_UNSUPPORTED;
+#endif
 }
 
 }  // extern "C"

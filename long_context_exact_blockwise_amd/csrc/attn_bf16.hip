@@ -376,6 +376,8 @@ __device__ __forceinline__ void fwd_bf16_body(AttnParams p, TableView t, int mod
   const int32_t* rg0 = t.q_range + (int64_t(b) * t.nqb + r0) * 2;
   int lo, hi;
   range_union(rg0, rg0 + 2, has_r1, lo, hi);
+  LWM_CHECK(r0 < t.nqb, kChkFwdRow);
+  LWM_CHECK(lo > hi || (lo >= 0 && hi < t.nkb), kChkFwdRange);
   if (kSplit) {
     const int s0 = int(blockIdx.y) * split_tiles;
     lo = max(lo, s0);
@@ -430,6 +432,8 @@ __device__ __forceinline__ void fwd_bf16_body(AttnParams p, TableView t, int mod
   auto step = [&](const uint16_t* kb_lds, const uint16_t* vb_lds, const int32_t* sb_lds,
                   uint16_t* kn_lds, uint16_t* vn_lds, int32_t* sn_lds) {
     const int st = st_c;
+    LWM_CHECK(kt >= c0 && kt <= c1 && kt >= lo && kt <= hi && kt * BK < p.Sk, kChkFwdTile);
+    LWM_CHECK(st == LWM_TILE_PARTIAL || st == LWM_TILE_FULL, kChkFwdStatus);
     const int kn = kn_c;
     // the next step's: statuses of tiles kn and kn + 1 (indices kept inside the chunk)
     const int st_n = stat_lds[min(kn, c1) - c0];
@@ -551,6 +555,7 @@ __device__ __forceinline__ void fwd_bf16_body(AttnParams p, TableView t, int mod
 
   const float l_tot = half_sum(l_run);
   if (!qlive) return;
+  LWM_CHECK(b < p.B, kChkFwdOut);
   const int64_t r64 = (kSplit ? int64_t(blockIdx.y) * p.B * p.H * p.Sq : 0) + bh * p.Sq + qrow;
   if (!kSplit && mode == LWM_OUT_FINAL) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -639,6 +644,7 @@ __global__ void __launch_bounds__(NT) decode_combine_kernel(int64_t rows, int ns
   const int rpb = (NT / 32) / gpr;  // rows per workgroup
   const int sub = grp % gpr;
   const int64_t nrb = (rows + rpb - 1) / rpb;
+  LWM_CHECK(gpr >= 1 && (NT / 32) % gpr == 0 && nsplit >= 1, kChkCombine);
   for (int64_t rb = blockIdx.x; rb < nrb; rb += gridDim.x) {
     const int64_t row = rb * rpb + grp / gpr;
     const bool live = row < rows;
@@ -778,6 +784,8 @@ __device__ __forceinline__ void dq_bf16_body(AttnParams p, TableView t, int nqt,
   const int32_t* rg0 = t.q_range + (int64_t(b) * t.nqb + r0) * 2;
   int lo, hi;
   range_union(rg0, rg0 + 2, has_r1, lo, hi);
+  LWM_CHECK(r0 < t.nqb, kChkDqRow);
+  LWM_CHECK(lo > hi || (lo >= 0 && hi < t.nkb), kChkDqRange);
   const uint8_t* st0 = t.status + (int64_t(b) * t.nqb + r0) * t.nkb;
   const uint8_t* st1 = st0 + t.nkb;
   const float c = p.scale * kLog2e;
@@ -796,6 +804,8 @@ __device__ __forceinline__ void dq_bf16_body(AttnParams p, TableView t, int nqt,
   auto step = [&](const uint16_t* kb_lds, const uint16_t* vb_lds, const int32_t* sb_lds,
                   uint16_t* kn_lds, uint16_t* vn_lds, int32_t* sn_lds) {
     const int st = uniform(stat_lds[kt - c0]);
+    LWM_CHECK(kt >= c0 && kt <= c1 && kt >= lo && kt <= hi && kt * BK < p.Sk, kChkDqTile);
+    LWM_CHECK(st == LWM_TILE_PARTIAL || st == LWM_TILE_FULL, kChkDqStatus);
     const int kn = next_live_lds(stat_lds, c0, kt + 1, c1);
     wait_vmem();
     __syncthreads();
@@ -1009,6 +1019,8 @@ __device__ __forceinline__ void dkv_bf16_body(AttnParams p, TableView t, int nkt
   const int32_t* rg0 = t.k_range + (int64_t(b) * t.nkb + c0) * 2;
   int lo, hi;
   range_union(rg0, rg0 + 2, has_c1, lo, hi);
+  LWM_CHECK(c0 < t.nkb, kChkDkvCol);
+  LWM_CHECK(lo > hi || (lo >= 0 && hi < t.nqb), kChkDkvRange);
   const uint8_t* stb = t.status + int64_t(b) * t.nqb * t.nkb;
   const float c = p.scale * kLog2e;
 
@@ -1038,6 +1050,8 @@ __device__ __forceinline__ void dkv_bf16_body(AttnParams p, TableView t, int nkt
   auto step = [&](const uint16_t* qb_lds, const uint16_t* gb_lds, const float* rb_lds,
                   uint16_t* qn_lds, uint16_t* gn_lds, float* rn_lds) {
     const int st = st_c;
+    LWM_CHECK(qb >= w0 && qb <= w1 && qb >= lo && qb <= hi && qb * TB < p.Sq, kChkDkvTile);
+    LWM_CHECK(st == LWM_TILE_PARTIAL || st == LWM_TILE_FULL, kChkDkvStatus);
     const int qn = qn_c;
     // the next step's: statuses of tiles qn and qn + 1 (indices kept inside the chunk)
     const int st_n = stat_lds[min(qn, w1) - w0];
@@ -1314,5 +1328,7 @@ hipError_t launch_bwd_bf16(const lwm_attn_desc& d, int phase, const void* q, con
         seg_k, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv));
   return hipGetLastError();
 }
+
+LWM_DEBUG_READER(attn_bf16)
 
 }  // namespace lwm

@@ -57,9 +57,11 @@ __global__ void __launch_bounds__(kBlk) fwd_f32_kernel(AttnParams p, TableView t
 
   const int32_t* rng = t.q_range + (int64_t(b) * t.nqb + qb) * 2;
   const int kb_lo = rng[0], kb_hi = rng[1];
+  LWM_CHECK(qb < t.nqb && (kb_lo > kb_hi || (kb_lo >= 0 && kb_hi < t.nkb)), kChkF32Range);
   const uint8_t* st_row = t.status + (int64_t(b) * t.nqb + qb) * t.nkb;
   for (int kb = kb_lo; kb <= kb_hi; ++kb) {
     const uint8_t st = st_row[kb];
+    LWM_CHECK(st <= LWM_TILE_FULL && kb * kBlk < p.Sk, kChkF32Tile);
     if (st == LWM_TILE_SKIP) continue;
     __syncthreads();
     for (int i = tid; i < kBlk * D; i += kBlk) {
@@ -159,9 +161,11 @@ __global__ void __launch_bounds__(kBlk) dq_f32_kernel(AttnParams p, TableView t,
   const int32_t sq = live ? seg_q[int64_t(b) * p.Sq + row] : -1;
   const int64_t qpos = p.q_offset + row;
   const int32_t* rng = t.q_range + (int64_t(b) * t.nqb + qb) * 2;
+  LWM_CHECK(qb < t.nqb && (rng[0] > rng[1] || (rng[0] >= 0 && rng[1] < t.nkb)), kChkF32Range);
   const uint8_t* st_row = t.status + (int64_t(b) * t.nqb + qb) * t.nkb;
   for (int kb = rng[0]; kb <= rng[1]; ++kb) {
     const uint8_t st = st_row[kb];
+    LWM_CHECK(st <= LWM_TILE_FULL && kb * kBlk < p.Sk, kChkF32Tile);
     if (st == LWM_TILE_SKIP) continue;
     __syncthreads();
     for (int i = tid; i < kBlk * D; i += kBlk) {
@@ -233,9 +237,11 @@ __global__ void __launch_bounds__(kBlk) dkv_f32_kernel(AttnParams p, TableView t
   const int32_t sk = live ? seg_k[int64_t(b) * p.Sk + key] : -2;
   const int64_t kpos = p.k_offset + key;
   const int32_t* rng = t.k_range + (int64_t(b) * t.nkb + kb) * 2;
+  LWM_CHECK(kb < t.nkb && (rng[0] > rng[1] || (rng[0] >= 0 && rng[1] < t.nqb)), kChkF32Range);
   const uint8_t* st_base = t.status + int64_t(b) * t.nqb * t.nkb + kb;
   for (int qb = rng[0]; qb <= rng[1]; ++qb) {
     const uint8_t st = st_base[int64_t(qb) * t.nkb];
+    LWM_CHECK(st <= LWM_TILE_FULL && qb * kBlk < p.Sq, kChkF32Tile);
     if (st == LWM_TILE_SKIP) continue;
     __syncthreads();
     for (int i = tid; i < kBlk * D; i += kBlk) {
@@ -335,5 +341,7 @@ hipError_t launch_bwd_f32(const lwm_attn_desc& d, int phase, const float* q, con
     default: return hipErrorInvalidValue;
   }
 }
+
+LWM_DEBUG_READER(attn_f32)
 
 }  // namespace lwm

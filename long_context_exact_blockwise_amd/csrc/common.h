@@ -18,6 +18,65 @@ struct TableLayout {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// ---- device checks (debug builds) ------------------------------------------------------
+// Built with LWM_DEBUG, the kernels check the indices they derive from the block table (the
+// query and key ranges, the tile statuses, the slots of the status chunk staged in LDS) and
+// from their launch shape against the extents they index.  A failed check does not trap: it
+// sets bit `code` of the first word of a device array private to its source file and, for the
+// first failure only, stores code << 24 | workgroup in the second; lwm_attn_debug_status reads
+// and clears every file's words.  Without LWM_DEBUG a check compiles to nothing.
+enum DebugCheck : unsigned {
+  kChkFwdRow = 1,      // forward / decode: the query tile's table rows exist
+  kChkFwdRange = 2,    // forward / decode: key range of those rows inside the table
+  kChkFwdTile = 3,     // forward / decode: visited key tile inside the range, chunk and keys
+  kChkFwdStatus = 4,   // forward / decode: visited tile's status is PARTIAL or FULL
+  kChkFwdOut = 5,      // forward / decode: output row inside the outputs
+  kChkDqRow = 6,       // dQ: the query tile's table rows exist
+  kChkDqRange = 7,     // dQ: key range inside the table
+  kChkDqTile = 8,      // dQ: visited key tile inside the range, chunk and keys
+  kChkDqStatus = 9,    // dQ: visited tile's status
+  kChkDkvCol = 10,     // dK/dV: the key tile's table columns exist
+  kChkDkvRange = 11,   // dK/dV: query range inside the table
+  kChkDkvTile = 12,    // dK/dV: visited query tile inside the range, chunk and queries
+  kChkDkvStatus = 13,  // dK/dV: visited tile's status
+  kChkCombine = 14,    // decode combine: row inside the outputs
+  kChkF32Range = 15,   // float32 kernels: table range inside the table
+  kChkF32Tile = 16,    // float32 kernels: visited tile inside the range and the sequence
+  kChkTable = 17,      // table builder: block index and status value in range
+  kChkMerge = 18,      // merge: row inside the states
+  kChkSelfTest = 31,   // set on request by lwm_attn_debug_status, to test the reporting
+};
+
+#ifdef LWM_DEBUG
+static __device__ unsigned int g_debug_words[2];
+__device__ __forceinline__ void debug_fail(unsigned code) {
+  atomicOr(&g_debug_words[0], 1u << code);
+  atomicCAS(&g_debug_words[1], 0u, (code << 24) | (blockIdx.x & 0xFFFFFFu));
+}
+#define LWM_CHECK(cond, code)                  \
+  do {                                         \
+    if (!(cond)) ::lwm::debug_fail(code);      \
+  } while (0)
+// Defines debug_read_<name>: copies this file's two words to w and clears them.
+#define LWM_DEBUG_READER(name)                                                            \
+  hipError_t debug_read_##name(unsigned* w) {                                            \
+    hipError_t e = hipMemcpyFromSymbol(w, HIP_SYMBOL(g_debug_words), 2 * sizeof(unsigned)); \
+    if (e != hipSuccess) return e;                                                        \
+    const unsigned z[2] = {0u, 0u};                                                       \
+    return hipMemcpyToSymbol(HIP_SYMBOL(g_debug_words), z, sizeof z);                     \
+  }
+hipError_t debug_read_attn_bf16(unsigned* w);
+hipError_t debug_read_attn_f32(unsigned* w);
+hipError_t debug_read_table(unsigned* w);
+hipError_t debug_read_merge(unsigned* w);
+hipError_t debug_read_api(unsigned* w);
+#else
+#define LWM_CHECK(cond, code) \
+  do {                        \
+  } while (0)
+#define LWM_DEBUG_READER(name)
+#endif
+
 inline TableLayout table_layout(const lwm_attn_desc& d) {
   TableLayout t;
   t.nqb = (d.Sq + d.block_q - 1) / d.block_q;

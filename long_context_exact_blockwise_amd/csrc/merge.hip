@@ -33,6 +33,8 @@ __global__ void __launch_bounds__(256) merge_kernel(int64_t rows, int32_t D, flo
   const int part = int(gid % q4);
   if (row >= rows) return;
   const float m1 = M[row], l1 = L[row];
+  // an empty state (no key seen) carries m = -inf and l = 0
+  LWM_CHECK(q4 * 4 == D && l1 >= 0.f && (m1 != -INFINITY || l1 == 0.f), kChkMerge);
   float4 a = reinterpret_cast<const float4*>(ACC + row * D)[part];
   float m = m1, l = l1;
   if (kHasChunk) {
@@ -92,5 +94,7 @@ hipError_t launch_merge(int64_t rows, int32_t D, float* m, float* l, float* acc,
   return bf ? go<false, true, true>(rows, D, m, l, acc, mc, lc, accc, o, lse, stream)
             : go<false, true, false>(rows, D, m, l, acc, mc, lc, accc, o, lse, stream);
 }
+
+LWM_DEBUG_READER(merge)
 
 }  // namespace lwm

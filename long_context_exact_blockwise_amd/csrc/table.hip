@@ -79,6 +79,7 @@ __global__ void __launch_bounds__(256) classify_kernel(AttnParams p, int32_t blo
     const bool one_segment = qs[0] == qs[1] && ks[0] == ks[1] && qs[0] == ks[0] && qs[0] >= 0;
     st = (whole && causal_full && one_segment) ? LWM_TILE_FULL : LWM_TILE_PARTIAL;
   }
+  LWM_CHECK(b < p.B && qb < nqb && kb < nkb, kChkTable);
   status[idx] = st;
 }
 
@@ -112,6 +113,7 @@ __global__ void __launch_bounds__(256) ranges_kernel(const uint8_t* __restrict__
   }
   lo = wave_min(lo);
   hi = wave_max(hi);
+  LWM_CHECK(hi < (wave < nrows ? nkb : nqb), kChkTable);
   if (lane == 0) {
     int32_t* out = wave < nrows ? q_range + wave * 2 : k_range + (wave - nrows) * 2;
     out[0] = hi < 0 ? 0 : lo;
@@ -163,5 +165,7 @@ hipError_t launch_build_table(const lwm_attn_desc& d, const int32_t* seg_q, cons
         status, d.B, L.nqb, L.nkb, q_range, k_range);
   return hipGetLastError();
 }
+
+LWM_DEBUG_READER(table)
 
 }  // namespace lwm

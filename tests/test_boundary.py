@@ -360,3 +360,25 @@ def test_rope_at_load_rejects_bad_arguments(lib):
     assert cb(desc(), kr=FAKE + 4) == ALIGN
     assert cb(desc(), ws=None) == WS
     assert cb(desc(), ws_bytes=lwm.lwm_attn_bwd_workspace_bytes(desc()) - 1) == WS
+
+
+def test_debug_status_in_normal_and_debug_builds(lib):
+    """The normal build has no device checks (LWM_ERR_UNSUPPORTED, words zeroed); both builds
+    reject a NULL words pointer and unknown flags before any HIP call.  The debug build
+    exports the same symbols."""
+    w = (ctypes.c_uint32 * 2)(7, 7)
+    assert lib.lwm_attn_debug_status(w, 0) == UNSUP
+    assert list(w) == [0, 0]
+    assert lib.lwm_attn_debug_status(None, 0) == INVALID
+    if not os.path.exists(lwm.DEBUG_LIB_PATH):
+        lwm_build.build()
+    dbg = lwm._open_library(lwm.DEBUG_LIB_PATH)
+    for name in header_functions():
+        assert hasattr(dbg, name), name
+    assert dbg.lwm_attn_debug_status(None, 0) == INVALID
+    assert dbg.lwm_attn_debug_status(w, 2) == INVALID
+    assert dbg.lwm_attn_debug_status(w, -1) == INVALID
+    # argument checks are the same code in both builds
+    d = desc()
+    assert dbg.lwm_attn_fwd(ctypes.byref(d), 0, None, None, None, None, None, None, None, None,
+                            None, None, None, None) == INVALID
