@@ -23,9 +23,10 @@
  *     accumulator is float32 [B,H,Sq,D].  Segment ids are int32 [B,Sq] / [B,Sk], shared by
  *     all heads.  A negative segment id marks padding: it sees nothing and nothing sees it.
  *   - Every pointer is a device pointer owned by the caller; the library never allocates,
- *     frees or synchronises.  Its only mutable global state is the static device buffer of
- *     lwm_attn_decode_noalloc (one per GPU).  `stream` is a hipStream_t (NULL = the null
- *     stream); every call only enqueues work on it and returns.
+ *     frees or synchronises (lwm_attn_debug_status, a test aid, synchronises).  Its only
+ *     mutable global state is the static device buffer of lwm_attn_decode_noalloc (one per
+ *     GPU), and in the debug build the device-check records.  `stream` is a hipStream_t
+ *     (NULL = the null stream); every other call only enqueues work on it and returns.
  *   - Device pointers must be 16-byte aligned.  All arguments are validated on the host
  *     before anything is enqueued; on error nothing is enqueued.
  *   - Return value: LWM_OK (0) or a negative LWM_ERR_* code; lwm_attn_status_string()
