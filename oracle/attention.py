@@ -25,6 +25,10 @@ at global position k_offset + j:
 Gradient of the same map for an upstream dO (chain rule through softmax):
   dV_j = sum_i P_ij dO_i,  dP_ij = <dO_i, v_j>,  Delta_i = <dO_i, O_i>,
   dS_ij = P_ij (dP_ij - Delta_i),  dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i
+A backward that is handed the forward's stored output O' (rounded to the storage dtype) forms
+Delta_i = <dO_i, O'_i> from it; with c_i = <dO_i, O'_i - O_i> held fixed its dQ, dK are the
+exact gradients of sum_i <dO_i, O_i> - sum_i c_i LSE_i (d LSE_i / d s_ij = P_ij), and dV is
+unchanged.  backward(..., o=O') evaluates that; o=None uses the exact O.
 Partial state over a subset C of keys (a KV chunk), relative to a reference max m:
   m = max over visible j in C of s_ij,  l = sum exp(s_ij - m),  acc = sum exp(s_ij - m) v_j
   empty subset: (m, l, acc) = (-inf, 0, 0)
@@ -75,13 +79,15 @@ def forward_head(q, k, v, mask, scale):
     return o, lse, p
 
 
-def backward_head(q, k, v, do, mask, scale):
-    """(dQ, dK, dV) for one head, float64."""
+def backward_head(q, k, v, do, mask, scale, o=None):
+    """(dQ, dK, dV) for one head, float64.  o: the stored forward output Delta is formed
+    from (None: the exact output)."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     do = np.asarray(do, np.float64)
-    o, _, p = forward_head(q, k, v, mask, scale)
+    o_exact, _, p = forward_head(q, k, v, mask, scale)
+    o = o_exact if o is None else np.asarray(o, np.float64)
     dv = p.T @ do
     dp = do @ v.T
     delta = (do * o).sum(axis=1)
@@ -103,16 +109,18 @@ def forward(q, k, v, seg_q, seg_k, scale, causal=True, q_offset=0, k_offset=0):
     return o, lse
 
 
-def backward(q, k, v, do, seg_q, seg_k, scale, causal=True, q_offset=0, k_offset=0):
-    """Batched gradient; returns (dQ, dK, dV) in float64."""
+def backward(q, k, v, do, seg_q, seg_k, scale, causal=True, q_offset=0, k_offset=0, o=None):
+    """Batched gradient; returns (dQ, dK, dV) in float64.  o [B,H,Sq,D]: the stored forward
+    output the backward is handed (None: the exact output)."""
     dq = np.zeros(q.shape, np.float64)
     dk = np.zeros(k.shape, np.float64)
     dv = np.zeros(v.shape, np.float64)
     for b in range(q.shape[0]):
         mask = visibility(seg_q[b], seg_k[b], q_offset, k_offset, causal)
         for h in range(q.shape[1]):
-            dq[b, h], dk[b, h], dv[b, h] = backward_head(q[b, h], k[b, h], v[b, h], do[b, h],
-                                                          mask, scale)
+            args = (q[b, h], k[b, h], v[b, h], do[b, h], mask, scale)
+            dq[b, h], dk[b, h], dv[b, h] = (backward_head(*args) if o is None
+                                            else backward_head(*args, o=o[b, h]))
     return dq, dk, dv
 
 

@@ -337,3 +337,52 @@ def test_batch_rows_with_different_layouts(dt):
         check_grad(n, f64(g), r, dt)
     if dt == "bf16":
         assert errs[5] <= TOL_O[dt] and errs[6] <= TOL_LSE
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_rising_scores_rescale_every_tile(dt):
+    """Scores that grow along the keys of each packed sample: each whole 64-key tile raises a
+    row's running max by 1.3 times the lazy-update threshold (8 in log2 units), so the
+    forward rescales its accumulator at most steps (all but a row's first and, when its
+    diagonal sits early in a tile, its last).  Compared with the oracle element
+    by element.  The backward is handed the stored O and forms Delta = <dO, O> from it, so
+    its reference is the oracle's gradient given the same O: where a row's softmax sits on
+    a few keys, dP - Delta is a small difference and the rounding of a bf16 O moves it by a
+    visible share (with steeper slopes, LSE ~140, by about 8 % of max |dQ|)."""
+    D = 128 if dt == "bf16" else 64
+    S, H, seg_len = 1280, 2, 320
+    say(f"rising scores {dt}: S={S} H={H} D={D} samples of {seg_len}")
+    x, _, _ = make_case(51, 1, H, S, S, D, dt, "single")
+    seg = (np.arange(S) // seg_len).astype(np.int32)[None]
+    rng = np.random.default_rng(51)
+    q = rng.normal(0, 0.5, (1, H, S, D)).astype(np.float32)
+    k = rng.normal(0, 0.5, (1, H, S, D)).astype(np.float32)
+    # score slope per key: 1.3 x the threshold (8 log2 units) per 64-key tile
+    slope = 1.3 * 8 * math.log(2) * math.sqrt(D) / (40.0 * 64)
+    q[..., 0] = 40.0
+    k[..., 0] = slope * (np.arange(S) % seg_len)
+    for n, arr in (("q", q), ("k", k)):
+        x[n] = arr if dt == "f32" else li.bf16_bits_from_f32(arr)
+    scale = 1 / math.sqrt(D)
+    # the construction does what it is for: the running max jumps past the threshold at most
+    # tile steps
+    qh, kh, vh, doh = (host_f64(x[n], dt) for n in ("q", "k", "v", "do"))
+    mask = A.visibility(seg[0], seg[0])
+    s2 = np.where(mask, (qh[0, 0] @ kh[0, 0].T) * scale / math.log(2), -np.inf)
+    tile_max = np.stack([s2[:, t:t + 64].max(axis=1) for t in range(0, S, 64)], axis=1)
+    run_max = np.maximum.accumulate(tile_max, axis=1)
+    live = np.isfinite(tile_max[:, 1:]) & np.isfinite(run_max[:, :-1])
+    jumps = live & (tile_max[:, 1:] > run_max[:, :-1] + 8)
+    assert jumps.sum() > 0.6 * live.sum()
+    o_ref, lse_ref, _ = run_oracle(x, seg, seg, dt, scale, True, 0, 0, grads=False)
+    qd, kd, vd, dod = (to_dev(x[n], dt) for n in ("q", "k", "v", "do"))
+    sq = seg_dev(seg)
+    o, lse, table = lwm.attention_forward(qd, kd, vd, sq, sq)
+    dq, dk, dv = lwm.attention_backward(qd, kd, vd, o, dod, lse, sq, sq, table)
+    torch.cuda.synchronize()
+    eo, el = max_abs(f64(o), o_ref), max_abs(f64(lse), lse_ref)
+    say(f"  max |LSE| {np.abs(lse_ref).max():.1f}; max-abs O {eo:.2e} LSE {el:.2e}")
+    assert eo <= TOL_O[dt] and el <= TOL_LSE
+    ref = A.backward(qh, kh, vh, doh, seg, seg, scale, True, o=f64(o))
+    for n, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        check_grad(n, f64(g), r, dt)

@@ -54,6 +54,11 @@ def bwd_wrong_dv_operand(q, k, v, do, mask, scale):
     return dq, dk, p.T @ o
 
 
+def bwd_ignores_stored_o(q, k, v, do, mask, scale, o=None):
+    # Delta always from the exact output, whatever output the backward is handed
+    return _orig_backward_head(q, k, v, do, mask, scale)
+
+
 def merge_same_weight(a, b):
     m1, l1, acc1 = a
     m2, l2, acc2 = b
@@ -263,6 +268,7 @@ MUTANTS = [
     ("backward_head", bwd_drops_delta, [pins.test_finite_difference_gradients]),
     ("backward_head", bwd_unscaled_dk, [pins.test_finite_difference_gradients]),
     ("backward_head", bwd_wrong_dv_operand, [pins.test_finite_difference_gradients]),
+    ("backward_head", bwd_ignores_stored_o, [pins.test_stored_output_gradients_by_autograd]),
     ("merge_states", merge_same_weight, [pins.test_ring_order_merge_equals_full]),
     ("forward_head", fwd_lse_without_log,
      [lambda: pins.test_blockwise_equals_one_shot(64), lambda: pins.test_q_zero_gives_segment_prefix_mean(1)]),

@@ -411,6 +411,37 @@ def test_finite_difference_gradients():
             assert abs(fd - grad[i, d]) <= 1e-6 * max(1.0, abs(grad[i, d])), (name, i, d)
 
 
+def test_stored_output_gradients_by_autograd():
+    """A backward handed a stored (rounded) output O': with c_i = <dO_i, O'_i - O_i> held
+    fixed, its dQ and dK are torch autograd's float64 gradients of
+    sum_i <dO_i, O_i> - sum_i c_i LSE_i (O and LSE formed by torch from the masked scores),
+    and dV is unchanged; handed the exact O it gives the exact gradient."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(23)
+    S, D, H = 80, 16, 2
+    seg = li.segment_ids_from_lengths([30, 50])[None]
+    q, k, v, do = (rng.standard_normal((1, H, S, D)) for _ in range(4))
+    scale = 1 / math.sqrt(D)
+    o, _ = A.forward(q, k, v, seg, seg, scale, True)
+    exact = A.backward(q, k, v, do, seg, seg, scale, True)
+    for g0, g1 in zip(exact, A.backward(q, k, v, do, seg, seg, scale, True, o=o)):
+        assert np.max(np.abs(g0 - g1)) < 1e-13
+    o_st = o + 0.05 * rng.standard_normal(o.shape)
+    dq, dk, dv = A.backward(q, k, v, do, seg, seg, scale, True, o=o_st)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    mask = torch.tensor(A.visibility(seg[0], seg[0], causal=True))
+    s = (tq @ tk.transpose(-1, -2) * scale).masked_fill(~mask, float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    to = torch.exp(s - lse[..., None]) @ tv
+    c = torch.tensor((do * (o_st - o)).sum(axis=-1))
+    loss = (torch.tensor(do) * to).sum() - (c * lse).sum()
+    loss.backward()
+    for g, tg in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        assert np.max(np.abs(g - tg.numpy())) < 1e-12
+    # the stored output matters: the perturbation moves dQ
+    assert np.max(np.abs(dq - exact[0])) > 1e-3
+
+
 # --------------------------------------------------------------------------------------
 # 9. special cases that reduce to a library routine: torch SDPA in float64 on the CPU
 # --------------------------------------------------------------------------------------
