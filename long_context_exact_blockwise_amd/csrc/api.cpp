@@ -74,7 +74,7 @@ const char* lwm_attn_status_string(int status) {
   }
 }
 
-int lwm_attn_version(void) { return 200; }
+int lwm_attn_version(void) { return 300; }
 
 size_t lwm_attn_block_table_bytes(const lwm_attn_desc* d) {
   if (check_desc(d) != LWM_OK) return 0;
