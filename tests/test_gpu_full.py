@@ -3,9 +3,9 @@
 Outputs the oracle cannot form whole are checked on seeded sampled rows (each computed
 exactly from its full masked score row), on whole sampled segments (a packed segment
 attends only to itself, so the per-segment oracle is exact for it), on a 2048-token
-sub-instance, and on every row through the Q = 0 closed form (O = mean of V over the
+sub-instance, on every row through the Q = 0 closed form (O = mean of V over the
 visible keys, LSE = ln of their count), which checks the masks and the skip table
-exhaustively."""
+exhaustively, and on every head and segment through identities the exact gradient obeys."""
 import math
 
 import numpy as np
@@ -189,6 +189,44 @@ def test_packed_128k_fwd_bwd():
                 worst[i] = max(worst[i], check_grad(n, f64(g[0, h])[s:e], r, "bf16")[0])
     say(f"  whole segments {list(pick)} heads {list(heads)}: dQ {worst[0]:.2e} dK {worst[1]:.2e} dV {worst[2]:.2e}")
     assert max(worst) <= TOL_GRAD["bf16"]
+    check_gradient_identities(w, bounds, x, o, dq, dk, dv)
+
+
+def check_gradient_identities(w, bounds, x, o, dq, dk, dv):
+    """Identities of the exact gradient, on every head, segment and column at full size.
+    Each row's weights sum to one over keys of its own segment and each row's dS sums to
+    zero, so per segment sum_j dV_j = sum_i dO_i and sum_j dK_j = 0; and scaling q by c and
+    k by 1/c leaves the scores unchanged, so per head sum_i <dQ_i, q_i> = sum_j <dK_j, k_j>.
+    The GPU rounds P and dS to bf16 (relative 2^-9) before the products and its gradients to
+    bf16 at the end, so each side may differ by 2^-9 of the sum of the magnitudes involved;
+    the bars are twice that (2^-8)."""
+    seg_idx = torch.empty(w.Sq, dtype=torch.long, device="cuda")
+    for n, (s, e) in enumerate(bounds):
+        seg_idx[s:e] = n
+
+    def seg_sum(t):  # [B=1, H, S, D] -> float64 [segments, H, D]
+        out = torch.zeros((len(bounds), w.H, w.D), dtype=torch.float64, device="cuda")
+        return out.index_add_(0, seg_idx, t[0].double().transpose(0, 1))
+
+    sv, so = seg_sum(dv), seg_sum(x["do"])
+    tol_v = 2.0 ** -8 * (seg_sum(dv.abs()) + seg_sum(x["do"].abs())) + 1e-6
+    rv = float(((sv - so).abs() / tol_v).max())
+    sk = seg_sum(dk)
+    # dS rounding: |sum_j d dS_ij| <= 2^-9 sum_j |dS_ij| <= 2^-9 * 2 |dO_i| max_j |v_j| per row
+    rowfac = (x["do"].float().norm(dim=-1, keepdim=True) * x["q"].float().abs()).contiguous()
+    vnorm_max = torch.zeros((len(bounds), w.H), dtype=torch.float64, device="cuda")
+    vn = x["v"][0].float().norm(dim=-1).transpose(0, 1).double()  # [S, H]
+    vnorm_max = vnorm_max.index_reduce_(0, seg_idx, vn, "amax", include_self=False)
+    tol_k = 2.0 ** -8 * (seg_sum(dk.abs()) + w.scale * 2 * vnorm_max[..., None] * seg_sum(rowfac)) + 1e-6
+    rk = float((sk.abs() / tol_k).max())
+    lhs = (dq.double() * x["q"].double()).sum(dim=(2, 3))[0]
+    rhs = (dk.double() * x["k"].double()).sum(dim=(2, 3))[0]
+    mag = (dq.double() * x["q"].double()).abs().sum(dim=(2, 3))[0] + \
+        (dk.double() * x["k"].double()).abs().sum(dim=(2, 3))[0]
+    rq = float(((lhs - rhs).abs() / (2.0 ** -8 * mag)).max())
+    say(f"  identities on all {w.H} heads, {len(bounds)} segments (error / bar, at most 1): "
+        f"sum dV = sum dO {rv:.2e}, sum dK = 0 {rk:.2e}, <dQ, q> = <dK, k> {rq:.2e}")
+    assert rv <= 1 and rk <= 1 and rq <= 1
 
 
 def test_packed_128k_window_subinstance():
