@@ -482,7 +482,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the multi-GPU ring is not part of this build", file=sys.stderr)
+              "the library has no multi-GPU ring transfer: a run measures one GPU's share", file=sys.stderr)
         return 2
 
     import torch
