@@ -69,14 +69,24 @@ __global__ void __launch_bounds__(256) lds_probe(int iters, float* out) {
   out[blockIdx.x * blockDim.x + threadIdx.x] = float(acc ^ acc2);
 }
 
-// Streaming read of n uint4 (16 bytes each), grid-stride; one partial per thread to out
-// (gridDim.x * blockDim.x floats).
+// Streaming read of n uint4 (16 bytes each), grid-stride, four independent loads in flight
+// per lane (every index below n); one partial per thread to out (gridDim.x * blockDim.x
+// floats).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ void __launch_bounds__(256) read_probe(const u32x4* __restrict__ src, int64_t n, float* out) {
   uint32_t acc = 0;
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+  int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const u32x4 a = __builtin_nontemporal_load(src + i);
+    const u32x4 b = __builtin_nontemporal_load(src + i + stride);
+    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
+    const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
+    acc += (a[0] ^ a[1] ^ a[2] ^ a[3]) + (b[0] ^ b[1] ^ b[2] ^ b[3]) + (c[0] ^ c[1] ^ c[2] ^ c[3]) +
+           (d[0] ^ d[1] ^ d[2] ^ d[3]);
+  }
+  for (; i < n; i += stride) {
     const u32x4 v = __builtin_nontemporal_load(src + i);
     acc += v[0] ^ v[1] ^ v[2] ^ v[3];
   }
