@@ -386,3 +386,36 @@ def test_rising_scores_rescale_every_tile(dt):
     ref = A.backward(qh, kh, vh, doh, seg, seg, scale, True, o=f64(o))
     for n, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
         check_grad(n, f64(g), r, dt)
+
+
+def test_backward_phases_on_two_streams():
+    """The backward split into its phases: Delta on one stream, then dQ and dK/dV on two
+    further streams that wait for it, running side by side; the gradients equal those of
+    lwm_attn_bwd on one stream bit for bit (the phases share no scratch beyond Delta)."""
+    B, H, S, D = 1, 4, 3000, 128
+    say(f"backward phases on two streams: B={B} H={H} S={S}")
+    x, seg_q, seg_k = make_case(61, B, H, S, S, D, "bf16", "packed")
+    q, k, v, do = (to_dev(x[n], "bf16") for n in ("q", "k", "v", "do"))
+    sq = seg_dev(seg_q)
+    o, lse, table = lwm.attention_forward(q, k, v, sq, sq)
+    desc = lwm.make_desc(B, H, S, S, D, torch.bfloat16)
+    ws = torch.empty(lwm.lwm_attn_bwd_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    ref = [torch.empty_like(q) for _ in range(3)]
+    lwm.lwm_attn_bwd(desc, q, k, v, o, do, lse, sq, sq, table, *ref, ws)
+    torch.cuda.synchronize()
+    got = [torch.full_like(q, float("nan")) for _ in range(3)]
+    ws2 = torch.empty_like(ws)
+    s0, s1, s2 = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    s0.wait_stream(torch.cuda.current_stream())
+    lwm.lwm_attn_bwd_phase(desc, lwm.LWM_BWD_DELTA, q, k, v, o, do, lse, sq, sq, table, *got, ws2,
+                           stream=s0)
+    delta_done = torch.cuda.Event()
+    delta_done.record(s0)
+    for st, phase in ((s1, lwm.LWM_BWD_DQ), (s2, lwm.LWM_BWD_DKV)):
+        st.wait_event(delta_done)
+        lwm.lwm_attn_bwd_phase(desc, phase, q, k, v, o, do, lse, sq, sq, table, *got, ws2,
+                               stream=st)
+    torch.cuda.synchronize()
+    same = [bool(torch.equal(g, r)) for g, r in zip(got, ref)]
+    say(f"  dQ, dK, dV identical: {same}")
+    assert all(same)
