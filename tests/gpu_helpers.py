@@ -59,7 +59,8 @@ def max_abs(a, b):
     if a.size == 0:
         return 0.0
     both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
-    d = np.where(both_inf, 0.0, np.abs(a - b))
+    with np.errstate(invalid="ignore"):  # inf - inf on the pairs both_inf excludes
+        d = np.where(both_inf, 0.0, np.abs(a - b))
     return float(np.max(d))
 
 

@@ -214,9 +214,8 @@ def check_gradient_identities(w, bounds, x, o, dq, dk, dv):
     sk = seg_sum(dk)
     # dS rounding: |sum_j d dS_ij| <= 2^-9 sum_j |dS_ij| <= 2^-9 * 2 |dO_i| max_j |v_j| per row
     rowfac = (x["do"].float().norm(dim=-1, keepdim=True) * x["q"].float().abs()).contiguous()
-    vnorm_max = torch.zeros((len(bounds), w.H), dtype=torch.float64, device="cuda")
-    vn = x["v"][0].float().norm(dim=-1).transpose(0, 1).double()  # [S, H]
-    vnorm_max = vnorm_max.index_reduce_(0, seg_idx, vn, "amax", include_self=False)
+    vn = x["v"][0].float().norm(dim=-1).double()  # [H, S]
+    vnorm_max = torch.stack([vn[:, s:e].amax(dim=1) for s, e in bounds])  # [segments, H]
     tol_k = 2.0 ** -8 * (seg_sum(dk.abs()) + w.scale * 2 * vnorm_max[..., None] * seg_sum(rowfac)) + 1e-6
     rk = float((sk.abs() / tol_k).max())
     lhs = (dq.double() * x["q"].double()).sum(dim=(2, 3))[0]
