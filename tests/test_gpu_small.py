@@ -27,6 +27,12 @@ def make_case(seed, B, H, Sq, Sk, D, dtype, layout="packed", q_off=0, k_off=0, p
         ids = np.zeros(total, np.int32)
     elif layout == "packed":
         ids = pins.random_layout(rng, total, allow_padding=pad)
+    elif layout == "tiny_segments":
+        # many samples of one token (a row that sees only itself) among short ones, some of
+        # them crossing tile edges
+        pattern = [1, 1, 3, 1, 2, 1, 1, 63, 1, 1, 65, 1, 1, 1, 5, 130]
+        lengths = (pattern * (total // sum(pattern) + 1))
+        ids = li.segment_ids_from_lengths(lengths).astype(np.int32)[:total]
     elif layout.startswith("alternating"):
         # ids 0, 1, 0, 1, ... in runs of `run` tokens: a sample's tokens are not contiguous, so
         # SKIP tiles sit between live tiles of a row's (and a column's) range
@@ -64,6 +70,7 @@ CASES = [
     ("few_keys", 9, 1, 2, 130, 3, "single", 0, 0, False, False),
     ("alternating_tiles", 10, 1, 2, 1024, 1024, "alternating_128", 0, 0, True, False),
     ("alternating_ragged", 11, 1, 2, 900, 900, "alternating_100", 0, 0, True, False),
+    ("lone_segments", 12, 1, 2, 777, 777, "tiny_segments", 0, 0, True, False),
 ]
 
 
@@ -96,6 +103,18 @@ def test_bf16_forward_and_backward(case):
     assert eo <= TOL_O["bf16"] and el <= TOL_LSE
     for n, g, r in (("dQ", dq, dq_ref), ("dK", dk, dk_ref), ("dV", dv, dv_ref)):
         check_grad(n, f64(g), r, "bf16")
+    if layout == "tiny_segments":
+        # a one-token sample attends to itself alone: O_i = v_i, dQ_i = 0 and, no other row
+        # seeing its key, dV_i = dO_i and dK_i = 0
+        ids = seg_q[0]
+        lone = np.nonzero((np.r_[True, ids[1:] != ids[:-1]]) & (np.r_[ids[:-1] != ids[1:], True]))[0]
+        # (up to the bf16 rounding of O, which leaves dP - Delta = <dO, v - O> a few 1e-4)
+        say(f"  {lone.size} one-token samples")
+        assert lone.size >= 25
+        vv, dd = host_f64(x["v"], "bf16")[:, :, lone], host_f64(x["do"], "bf16")[:, :, lone]
+        assert np.all(np.abs(f64(o)[:, :, lone] - vv) <= 2.0 ** -8 * np.abs(vv))
+        assert np.all(np.abs(f64(dv)[:, :, lone] - dd) <= 2.0 ** -8 * np.abs(dd))
+        assert np.abs(f64(dq)[:, :, lone]).max() <= 1e-4 and np.abs(f64(dk)[:, :, lone]).max() <= 1e-4
 
 
 def test_tiny_packed_f32_forward_backward_partial():
