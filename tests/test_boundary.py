@@ -382,3 +382,23 @@ def test_debug_status_in_normal_and_debug_builds(lib):
     d = desc()
     assert dbg.lwm_attn_fwd(ctypes.byref(d), 0, None, None, None, None, None, None, None, None,
                             None, None, None, None) == INVALID
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """With no built library the package raises on the first call; there is no fallback."""
+    import subprocess
+    import sys
+
+    code = ("import long_context_exact_blockwise_amd as lwm\n"
+            "d = lwm.make_desc(1, 1, 64, 64, 128, lwm.LWM_BF16)\n"
+            "try:\n"
+            "    lwm.lwm_attn_block_table_bytes(d)\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n"
+            "    raise SystemExit(0)\n"
+            "raise SystemExit(3)\n")
+    env = dict(os.environ, LWM_ATTN_LIBRARY=str(tmp_path / "absent.so"))
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "not built" in r.stdout
