@@ -89,8 +89,8 @@ def load_library(path: str = LIB_PATH):
 
 @contextlib.contextmanager
 def active_library(path: str):
-    """Run the wrappers against another build of the library (the race-canary build) inside
-    a `with` block."""
+    """Run the wrappers against another build of the library (the race-canary build or the
+    build with device checks) inside a `with` block."""
     global _lib
     prev = _lib
     _lib = _open_library(path)
